@@ -1,0 +1,293 @@
+#!/usr/bin/env python3
+"""Throughput of the routed MoE layer on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+
+A step is one pass of the whole hot path over one batch of synthetic tokens:
+moe_route (router GEMV, top-6, gates) then moe_forward (histogram, prefix sum,
+scatter, [token quantisation], grouped up GEMM + ReLU^2, [intermediate
+quantisation], grouped down GEMM, combine); the stacked workload runs 23 such
+layers with pre-norm and residual.  Inputs are resident in HBM before timing.
+W untimed warm-up steps, then exactly K steps between two device
+synchronisations.  Per-stage durations come from HIP events recorded inside
+the timed steps on the stream the kernels run on.
+
+Prints one JSON line.  `roofline` describes the dominant kernel (algorithmic
+bytes or flops per launch / its mean duration); `cpu_baseline` is the CPU
+oracle timed on this host on a bounded sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "MoE-layer tokens/s; HBM GB/s at T=64, MFMA TFLOP/s at T=4096 (1 GPU)"
+HBM_PEAK_GBS = 8000.0
+MFMA_PEAK_TFLOPS = {"bf16": 2500.0, "fp8": 5000.0, "nvfp4": 2500.0}  # nvfp4 runs on bf16 MFMA
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=50)
+    p.add_argument("--warmup", type=int, default=5)
+    p.add_argument("--workload", default="decode_t64_bf16")
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--copy-calibration", action="store_true",
+                   help="only run a plain 1 GiB device copy (reference for HBM byte counters)")
+    return p.parse_args()
+
+
+class Hip:
+    """The few HIP runtime calls the timing needs (events)."""
+
+    def __init__(self):
+        self.lib = ctypes.CDLL("libamdhip64.so")
+        self.lib.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        self.lib.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
+        self.lib.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p,
+                                                 ctypes.c_void_p]
+        self.lib.hipEventDestroy.argtypes = [ctypes.c_void_p]
+
+    def event(self):
+        e = ctypes.c_void_p()
+        assert self.lib.hipEventCreate(ctypes.byref(e)) == 0
+        return e.value
+
+    def record(self, ev, stream):
+        assert self.lib.hipEventRecord(ctypes.c_void_p(ev), ctypes.c_void_p(stream)) == 0
+
+    def elapsed(self, a, b) -> float:
+        ms = ctypes.c_float()
+        assert self.lib.hipEventElapsedTime(ctypes.byref(ms), ctypes.c_void_p(a), ctypes.c_void_p(b)) == 0
+        return ms.value
+
+    def destroy(self, ev):
+        self.lib.hipEventDestroy(ctypes.c_void_p(ev))
+
+
+def weight_bytes_per_expert(fmt, F, H):
+    n = F * H
+    if fmt == "bf16":
+        return 2 * n
+    if fmt == "fp8":
+        return n + 4
+    return n // 2 + n // 16 + 4
+
+
+def main():
+    args = parse()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus > 1 or world > 1:
+        print(f"bench.py: this build measures one GPU only; --gpus {max(args.gpus, world)} "
+              "is not supported (the expert-parallel split is described in DESIGN.md)",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import sparse_moe_routed_amd as moe
+    from sparse_moe_routed_amd import synth
+
+    if args.copy_calibration:
+        n = 1 << 30
+        src = torch.ones(n, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(args.steps):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calibration_bytes_each_way": n, "launches": args.steps}), flush=True)
+        return
+
+    if args.workload not in synth.WORKLOADS:
+        sys.exit(f"unknown workload {args.workload}; choose from {sorted(synth.WORKLOADS)}")
+    wl = synth.WORKLOADS[args.workload]
+    T, fmt, n_layers = wl["T"], wl["fmt"], wl["layers"]
+    dims = synth.Dims()
+    ld = moe.LayerDims()
+    H, F, E, k = dims.hidden, dims.ffn, dims.n_experts, dims.top_k
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    dev = torch.device("cuda:0")
+    hip = Hip()
+
+    # ---------------------------------------------------------------- inputs
+    t_setup = time.time()
+    layers = []
+    for l in range(n_layers):
+        w_r, b = synth.make_router(l)
+        up, down = synth.make_experts(l)
+        up_d, down_d = up.to(dev), down.to(dev)
+        del up, down
+        bank = moe.quantize_experts(up_d, down_d, fmt, ld)
+        if fmt != "bf16":
+            del up_d, down_d
+        layers.append(dict(w_r=w_r.to(dev), b=b.to(dev), bank=bank))
+        print(f"# layer {l} ready ({time.time() - t_setup:.1f}s)", file=sys.stderr, flush=True)
+    x0 = synth.make_tokens(T, outliers=wl["outliers"]).to(dev)
+    ws = moe.workspace(ld, fmt, T, dev)
+    y = torch.empty((T, H), dtype=torch.float32, device=dev)
+    ids = torch.empty((T, k), dtype=torch.int32, device=dev)
+    gates = torch.empty((T, k), dtype=torch.float32, device=dev)
+    xin = torch.empty_like(x0)
+    xs = x0.clone()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream().cuda_stream
+    n_ev = moe.N_STAGES + 1
+
+    def step(ev_route=None, ev_stages=None):
+        if n_layers == 1:
+            if ev_route:
+                hip.record(ev_route[0], stream)
+            moe.route(x0, layers[0]["w_r"], layers[0]["b"], ld, ids=ids, gates=gates)
+            if ev_route:
+                hip.record(ev_route[1], stream)
+            if ev_stages:
+                moe.forward_timed(x0, ids, gates, layers[0]["bank"], ev_stages, ld, ws=ws, y=y)
+            else:
+                moe.forward(x0, ids, gates, layers[0]["bank"], ld, ws=ws, y=y)
+        else:
+            xs.copy_(x0)
+            for L in layers:
+                moe.prenorm(xs, xin)
+                moe.route(xin, L["w_r"], L["b"], ld, ids=ids, gates=gates)
+                moe.forward(xin, ids, gates, L["bank"], ld, ws=ws, y=y)
+                moe.residual_add(xs, y)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    # pass 1 (headline): exactly K steps between two synchronisations, no events
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_per_step = wall * 1e3 / args.steps
+    tokens_per_s = T * args.steps / wall
+
+    # pass 2 (attribution): K more steps with HIP events at every stage
+    # boundary, recorded on the stream the kernels run on (events add a few
+    # microseconds per step, so pass 1 alone gives the headline)
+    timed_stages = n_layers == 1
+    stage_ms = {}
+    if timed_stages:
+        ev_r = [[hip.event(), hip.event()] for _ in range(args.steps)]
+        ev_s = [[hip.event() for _ in range(n_ev)] for _ in range(args.steps)]
+        torch.cuda.synchronize()
+        for i in range(args.steps):
+            step(ev_r[i], ev_s[i])
+        torch.cuda.synchronize()
+        stage_ms["route"] = float(np.mean([hip.elapsed(a, b) for a, b in ev_r]))
+        for si, name in enumerate(moe.STAGES):
+            stage_ms[name] = float(np.mean([hip.elapsed(e[si], e[si + 1]) for e in ev_s]))
+        for e in ev_r + ev_s:
+            for h in e:
+                hip.destroy(h)
+
+    # ---------------------------------------------------------------- roofline
+    ids_h = ids.cpu().numpy()
+    touched = int(np.unique(ids_h).size)
+    R = T * k
+    wbe = weight_bytes_per_expert(fmt, F, H)
+    act_in_bytes = {"bf16": 2, "fp8": 1, "nvfp4": 2}[fmt]
+    layer_bytes = touched * 2 * wbe + E * H * 4 + E * 4 + T * H * 2 + T * H * 4
+    flops_up = 2.0 * R * F * H
+    roof = None
+    if timed_stages:
+        dom = "up" if stage_ms["up"] >= stage_ms["down"] else "down"
+        dur_s = stage_ms[dom] * 1e-3
+        if T <= 256:
+            # weight-streaming launch: bytes of the touched experts' panels plus
+            # its activation input and output
+            if dom == "up":
+                alg = touched * wbe + T * H * act_in_bytes + R * F * 2
+            else:
+                alg = touched * wbe + R * F * act_in_bytes + R * H * 4
+            achieved = alg / dur_s / 1e9
+            roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
+                    "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                    "traffic": None, "kernel": f"grouped_gemm_{dom}", "alg_bytes": int(alg)}
+        else:
+            achieved = flops_up / dur_s / 1e12
+            peak = MFMA_PEAK_TFLOPS[fmt]
+            roof = {"bound": "mfma", "achieved": round(achieved, 1), "peak": peak,
+                    "unit": "TFLOP/s", "frac": round(achieved / peak, 4), "traffic": None,
+                    "kernel": f"grouped_gemm_{dom}", "alg_flops": flops_up}
+        tf = os.path.join(ROOT, "profiles", f"traffic_{args.workload}.json")
+        if os.path.exists(tf):
+            rec = json.load(open(tf))
+            src = open(os.path.join(ROOT, "sparse_moe_routed_amd", "csrc", "gemm.hip"), "rb").read()
+            if rec.get("kernel") == roof["kernel"] and rec.get("source_sha256") == hashlib.sha256(src).hexdigest():
+                roof["traffic"] = rec["bytes_per_launch"]
+
+    layer_ms = ms_per_step / n_layers
+    out = {
+        "metric": METRIC,
+        "value": round(tokens_per_s, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": fmt,
+        "data": "synthetic (seeded; shapes and distributions of the Nemotron 3.5 Transcribe routed MoE layer)",
+        "config": {"workload": args.workload, "T": T, "hidden": H, "ffn": F, "experts": E,
+                   "top_k": k, "format": fmt, "layers": n_layers},
+        "layer_hbm_gbs": round(layer_bytes / (layer_ms * 1e-3) / 1e9, 1),
+        "layer_tflops": round(2 * flops_up / (layer_ms * 1e-3) / 1e12, 2),
+        "experts_touched": touched,
+        "stage_ms": {k2: round(v, 4) for k2, v in stage_ms.items()},
+        "roofline": roof,
+    }
+
+    # ---------------------------------------------------------------- CPU oracle
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(args, wl, dims)
+    print(json.dumps(out), flush=True)
+
+
+def cpu_baseline(args, wl, dims):
+    """The oracle as it stands, on a bounded token sample of the same workload."""
+    import numpy as np
+    from threadpoolctl import threadpool_info
+
+    from oracle import moe as om
+    from sparse_moe_routed_amd import synth
+
+    T = wl["T"]
+    x = synth.make_tokens(T, outliers=wl["outliers"]).float().numpy()
+    w_r, b = synth.make_router(0)
+    up, down = synth.make_experts(0)
+    bank = om.ExpertBank(up, down, wl["fmt"])
+    # bf16: the whole batch; fp8/nvfp4: the oracle re-quantises every touched
+    # expert on each call, so a few tokens already cost tens of seconds
+    n = T if wl["fmt"] == "bf16" else min(T, 4)
+    xs = x[:n]
+    t0 = time.perf_counter()
+    ids, g, _, _ = om.route(xs, w_r.numpy(), b.numpy(), dims.top_k)
+    om.forward(xs, ids, g, bank)
+    spent = time.perf_counter() - t0
+    done_tokens = n
+    threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    return {"value": round(done_tokens / spent, 3), "unit": "tokens/s", "cores": int(threads),
+            "kind": "oracle",
+            "sample": f"{done_tokens} tokens of the {T}-token batch (float64 NumPy, one layer, "
+                      f"{wl['fmt']} weights dequantised by the oracle), {spent:.1f}s"}
+
+
+if __name__ == "__main__":
+    main()

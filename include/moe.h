@@ -1,0 +1,207 @@
+/*
+ * moe.h -- C ABI of libmoe.so: the routed mixture-of-experts layer of the
+ * Nemotron 3.5 Transcribe hybrid decoder on AMD Instinct MI355X (gfx950).
+ *
+ * The layer (bloomery issue #967 "model: Nemotron 3.5 Transcribe from
+ * safetensors on x86 cards and DGX Spark", section 2 "Checkpoint facts";
+ * section 3 "Existing owners and gaps"):
+ *   width H = 2688, E = 128 experts, top-k = 6 routing, ungated ReLU^2 experts
+ *   of width F = 1856 (an up part H->F and a down part F->H, no gate matrix);
+ *   expert weights in BF16, FP8 (scalar-scale E4M3, W8A8) or 4-bit NVFP4
+ *   (W4A4).
+ * Routing is a separate formula from expert execution (audio.cpp port notes
+ * "NVIDIA Nemotron 3.5 Transcribe", section "CPU weight offload"), hence two
+ * calls: moe_route and moe_forward.
+ *
+ * Conventions for every call:
+ *   - Pointers marked [dev] are device pointers (hipMalloc or torch CUDA
+ *     tensors); [host] are host pointers read during the call only.
+ *   - All device work is enqueued asynchronously on `stream` (a hipStream_t;
+ *     NULL = the null stream).  No call synchronises with the host.
+ *   - Row-major, contiguous layouts; bf16 is passed as raw 16-bit words.
+ *   - The caller owns every buffer.  The library allocates no device memory;
+ *     scratch comes from the caller's workspace (moe_workspace_size).
+ *   - Arguments are validated on the host before any launch.  On error the
+ *     call returns a non-zero moe_status and enqueues nothing.  T == 0 is a
+ *     valid no-op.  A failed launch returns MOE_EHIP.
+ *   - Calls are reentrant; calls that share a workspace must be ordered on
+ *     one stream.  Non-finite inputs give undefined (but memory-safe)
+ *     results.  Expert ids outside [0, E) are dropped by moe_forward (their
+ *     slot contributes nothing).
+ *   - Supported shapes: 64 <= H, 64 <= F with H % 64 == F % 64 == 0,
+ *     16 <= E <= 256 with E % 16 == 0, 1 <= top_k <= min(8, E),
+ *     0 <= T <= 1 << 20.
+ */
+#ifndef MOE_H
+#define MOE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MOE_ABI_VERSION 1
+
+typedef enum {
+  MOE_OK = 0,
+  MOE_EINVAL = 1,       /* bad argument: null pointer, bad size or enum   */
+  MOE_EUNSUPPORTED = 2, /* valid request outside the supported shapes    */
+  MOE_EWORKSPACE = 3,   /* workspace missing or smaller than required    */
+  MOE_EHIP = 4          /* a HIP launch or runtime call failed           */
+} moe_status;
+
+/* Expert weight formats (bloomery issue #967, section 2 "Checkpoint facts":
+ * BF16, FP8 scalar-scale E4M3 W8A8, NVFP4 W4A4 experts). */
+typedef enum {
+  MOE_WFMT_BF16 = 0,
+  MOE_WFMT_FP8 = 1,   /* E4M3 codes, one fp32 scale per expert projection;
+                         activations quantised per tensor to E4M3          */
+  MOE_WFMT_NVFP4 = 2  /* E2M1 codes in 16-element blocks along K, one E4M3
+                         scale per block, one fp32 scale per expert
+                         projection; activations quantised the same way    */
+} moe_wfmt;
+
+typedef enum { MOE_Y_BF16 = 0, MOE_Y_F32 = 1 } moe_ydtype;
+
+/* [host] layer shape: hidden H, expert width F, experts E, experts per token k */
+typedef struct {
+  int32_t hidden, ffn, n_experts, top_k;
+} moe_dims;
+
+/* [host] struct of [dev] router tensors: w fp32 [E, H]; bias fp32 [E] or NULL */
+typedef struct {
+  const float* w;
+  const float* bias;
+} moe_router;
+
+/* [host] struct of [dev] expert bank pointers.
+ *   BF16 : up  bf16 [E, F, H],  down bf16 [E, H, F]
+ *   FP8  : up  u8 E4M3 [E, F, H], down u8 [E, H, F]; up_s/down_s fp32 [E]
+ *          (weight = dec(code) * s)
+ *   NVFP4: up  u8 [E, F, H/2],  down u8 [E, H, F/2]  (two E2M1 codes per byte,
+ *          element 2i in the low nibble); up_bs u8 E4M3 [E, F, H/16],
+ *          down_bs [E, H, F/16]; up_s/down_s fp32 [E]
+ *          (weight = dec(code) * dec(block scale) * s)
+ * Unused pointers may be NULL. */
+typedef struct {
+  int32_t fmt; /* moe_wfmt */
+  const void* up;
+  const void* down;
+  const uint8_t* up_bs;
+  const uint8_t* down_bs;
+  const float* up_s;
+  const float* down_s;
+} moe_experts;
+
+/* MOE_ABI_VERSION of the built library. */
+int32_t moe_abi_version(void);
+
+/* Static, human-readable name of a status code (never NULL). */
+const char* moe_status_str(int32_t status);
+
+/* Bytes of workspace moe_forward needs for up to `max_tokens` tokens with
+ * weight format `fmt`; 0 for invalid arguments.  The workspace must be
+ * 256-byte aligned (hipMalloc and torch allocations are). */
+size_t moe_workspace_size(const moe_dims* dims, int32_t fmt, int32_t max_tokens);
+
+/* Router (bloomery issue #967, section 2: top-6 routing over 128 experts;
+ * audio.cpp notes, section "CPU weight offload": routing weights are their own
+ * formula).  For each token t:
+ *   l_t = fp32(x_t) . W_r^T + b                (fp32 accumulation)
+ *   ids[t, 0..k) = the k largest l_t,e, ordered by (logit desc, index asc)
+ *   gates[t, j]  = exp(l_t,ids[j]) / sum_j' exp(l_t,ids[j'])
+ * x [dev] bf16 [T, H]; ids [dev] int32 [T, k] out; gates [dev] fp32 [T, k] out. */
+int32_t moe_route(const moe_dims* dims, int32_t T, const void* x,
+                  const moe_router* router, int32_t* ids, float* gates,
+                  void* stream);
+
+/* Expert part of the layer (bloomery issue #967, sections 2-3: ungated ReLU^2
+ * experts 2688 -> 1856 -> 2688; audio.cpp notes, "CPU weight offload":
+ * grouped expert matrix multiplication).  For each token t:
+ *   y_t = sum_{j<k} gates[t,j] * W_down,e . a~,   a = bf16(relu(W_up,e . x~_t)^2)
+ * with e = ids[t, j], x~ / a~ the activations as the weight format quantises
+ * them (identity for BF16; per-tensor E4M3 for FP8; NVFP4 blocks for 4-bit),
+ * fp32 accumulation, slots summed in order j = 0..k-1.
+ *   x     [dev] bf16 [T, H]        ids [dev] int32 [T, k]    gates [dev] fp32 [T, k]
+ *   y     [dev] [T, H], bf16 (MOE_Y_BF16) or fp32 (MOE_Y_F32), written in full
+ *   ws    [dev] workspace of ws_bytes >= moe_workspace_size(dims, fmt, T)
+ * After the call the workspace holds the stage results described by
+ * moe_workspace_layout until the next call that uses it. */
+int32_t moe_forward(const moe_dims* dims, int32_t T, const void* x,
+                    const int32_t* ids, const float* gates,
+                    const moe_experts* experts, void* y, int32_t y_dtype,
+                    void* ws, size_t ws_bytes, void* stream);
+
+/* moe_forward with stage timing.  `events` [host] holds n_events >= 7
+ * hipEvent_t handles created by the caller; events[i] is recorded on `stream`
+ * before stage i and events[6] after the last one.  Stages: 0 permutation
+ * (histogram, prefix sum, scatter), 1 token quantisation (FP8/NVFP4), 2 up
+ * projection + ReLU^2, 3 intermediate quantisation (FP8/NVFP4), 4 down
+ * projection, 5 combine.  Results are identical to moe_forward. */
+#define MOE_N_STAGES 6
+int32_t moe_forward_timed(const moe_dims* dims, int32_t T, const void* x,
+                          const int32_t* ids, const float* gates,
+                          const moe_experts* experts, void* y, int32_t y_dtype,
+                          void* ws, size_t ws_bytes, void* stream,
+                          void* const* events, int32_t n_events);
+
+/* Byte offsets of stage results inside a moe_forward workspace (for tests and
+ * tools; -1 where a stage does not exist for the format). */
+typedef struct {
+  int64_t counts;     /* int32 [E]: rows routed to each expert               */
+  int64_t offsets;    /* int32 [E+1]: exclusive prefix sum of counts         */
+  int64_t sorted_src; /* int32 [T*k]: flat (t*k + j) index of each sorted row */
+  int64_t inv;        /* int32 [T*k]: sorted row of each flat index, -1 = dropped */
+  int64_t act;        /* bf16 [T*k, F]: a = bf16(relu(h)^2), sorted row order */
+  int64_t out_rows;   /* fp32 [T*k, H]: gate * W_down a~, sorted row order   */
+  int64_t x_q;        /* FP8: u8 [T, H] codes; NVFP4: bf16 [T, H] dequantised
+                         block values dec(q)*dec(sb) (tensor scale excluded) */
+  int64_t act_q;      /* FP8: u8 [T*k, F] codes; NVFP4: in place over act    */
+  int64_t scales;     /* fp32 [4]: x scale, act scale, amax(x), amax(act)    */
+  int64_t total;      /* bytes                                               */
+} moe_ws_layout;
+
+int32_t moe_workspace_layout(const moe_dims* dims, int32_t fmt, int32_t T,
+                             moe_ws_layout* out /* [host] */);
+
+/* Pack a bf16 expert bank into FP8 or NVFP4 on the device, one fp32 scale per
+ * expert projection (recipes: s = f32(amax/448), code = E4M3(f32(w*f32(448/amax)))
+ * for FP8; S = f32(amax/2688), block scale sb = E4M3(f32(amax_b/f32(6S))),
+ * code = E2M1(f32(w*f32(1/f32(sb*S)))) for NVFP4; amax == 0 -> zero codes and
+ * scale).  Layouts as in moe_experts.
+ *   up_bf16 [dev] [E, F, H], down_bf16 [dev] [E, H, F]
+ *   up_q, down_q [dev] out; up_bs, down_bs [dev] out (NVFP4 only, else NULL);
+ *   up_s, down_s [dev] fp32 [E] out. */
+int32_t moe_quantize_experts(const moe_dims* dims, int32_t fmt,
+                             const void* up_bf16, const void* down_bf16,
+                             void* up_q, void* down_q, uint8_t* up_bs,
+                             uint8_t* down_bs, float* up_s, float* down_s,
+                             void* stream);
+
+/* Per-tensor activation quantiser of moe_forward as a standalone call (same
+ * recipes as moe_quantize_experts, amax over the whole [rows, cols] tensor).
+ *   x [dev] bf16 [rows, cols]; codes [dev] u8 [rows, cols] (FP8) or
+ *   [rows, cols/2] (NVFP4, packed like the weights); bs [dev] u8
+ *   [rows, cols/16] (NVFP4 only); scale [dev] fp32 [1] out;
+ *   ws [dev] >= 256 bytes of scratch. */
+int32_t moe_quantize_activation(int32_t fmt, int32_t rows, int32_t cols,
+                                const void* x, void* codes, uint8_t* bs,
+                                float* scale, void* ws, size_t ws_bytes,
+                                void* stream);
+
+/* Stacked-path helpers.  The pages' model normalises around its layers
+ * (audio.cpp notes, section "Q4_K, Q3_K and Q2_K expert profiles": routing and
+ * normalisation stay unchanged); a weightless RMS pre-norm is used:
+ *   moe_prenorm:      out_t = bf16(x_t / sqrt(mean(x_t^2) + 1e-6))
+ *   moe_residual_add: x_t   = bf16(x_t + y_t)
+ * x, out [dev] bf16 [T, H]; y [dev] fp32 [T, H]. */
+int32_t moe_prenorm(int32_t T, int32_t H, const void* x, void* out, void* stream);
+int32_t moe_residual_add(int32_t T, int32_t H, void* x, const float* y, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_H */

@@ -81,6 +81,7 @@ class ExpertBank:
         self.fmt = fmt
         self._up = up_bf16
         self._down = down_bf16
+        self._pre = {}
 
     @staticmethod
     def _f64(t):
@@ -100,11 +101,31 @@ class ExpertBank:
 
     def up(self, e: int) -> np.ndarray:
         """Dequantised W_up of expert e, float64 [F, H]."""
+        if ("up", e) in self._pre:
+            return self._pre[("up", e)]
         return self._deq(self._up[e])
 
     def down(self, e: int) -> np.ndarray:
         """Dequantised W_down of expert e, float64 [H, F]."""
+        if ("down", e) in self._pre:
+            return self._pre[("down", e)]
         return self._deq(self._down[e])
+
+    def preload(self, experts, threads: int = 8):
+        """Dequantise the given experts up front on a thread pool (the same
+        arithmetic as up()/down(); used by tests to save wall time)."""
+        from concurrent.futures import ThreadPoolExecutor
+        jobs = [(kind, int(e)) for e in experts for kind in ("up", "down")]
+
+        def one(job):
+            kind, e = job
+            src = self._up if kind == "up" else self._down
+            return job, self._deq(src[e])
+
+        with ThreadPoolExecutor(max(1, threads)) as ex:
+            for job, arr in ex.map(one, jobs):
+                self._pre[job] = arr
+        return self
 
 
 def quantise_activation(v, fmt: str) -> np.ndarray:

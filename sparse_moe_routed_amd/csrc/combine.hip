@@ -1,0 +1,102 @@
+// Gate-weighted combine of the per-slot expert rows, plus the stacked-path
+// helpers (weightless RMS pre-norm and residual add).
+//
+// The down GEMM has already multiplied each sorted row by its gate, so the
+// combine gathers the k rows of a token in slot order j = 0..k-1 and adds
+// them in fp32: a deterministic gather, no atomics.  The routing weights are
+// their own formula (audio.cpp notes "NVIDIA Nemotron 3.5 Transcribe",
+// section "CPU weight offload").
+#include "moe_common.h"
+#include "moe_internal.h"
+
+namespace moe {
+
+namespace {
+
+constexpr int kCThreads = 256;
+
+__global__ __launch_bounds__(kCThreads) void combine_kernel(const float* __restrict__ rows,
+                                                            const int32_t* __restrict__ inv,
+                                                            int k, int H, void* y, int y_f32) {
+  const int t = blockIdx.x;
+  int src[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) src[j] = j < k ? inv[static_cast<size_t>(t) * k + j] : -1;
+  const int h4 = H / 4;
+  for (int c = threadIdx.x; c < h4; c += kCThreads) {
+    f32x4 s = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      if (src[j] >= 0) s += reinterpret_cast<const f32x4*>(rows + static_cast<size_t>(src[j]) * H)[c];
+    }
+    if (y_f32) {
+      reinterpret_cast<f32x4*>(static_cast<float*>(y) + static_cast<size_t>(t) * H)[c] = s;
+    } else {
+      const uint32_t lo = f32_to_bf16(s[0]) | (static_cast<uint32_t>(f32_to_bf16(s[1])) << 16);
+      const uint32_t hi = f32_to_bf16(s[2]) | (static_cast<uint32_t>(f32_to_bf16(s[3])) << 16);
+      reinterpret_cast<uint2*>(static_cast<uint16_t*>(y) + static_cast<size_t>(t) * H)[c] =
+          make_uint2(lo, hi);
+    }
+  }
+}
+
+// out = bf16(x / sqrt(mean(x^2) + 1e-6)), evaluated in double and rounded once
+__global__ __launch_bounds__(kCThreads) void prenorm_kernel(const uint16_t* __restrict__ x, int H,
+                                                            uint16_t* __restrict__ out) {
+  __shared__ double part[kCThreads / 64];
+  const int t = blockIdx.x;
+  const uint16_t* xr = x + static_cast<size_t>(t) * H;
+  double ss = 0.0;
+  for (int c = threadIdx.x; c < H; c += kCThreads) {
+    const double v = bf16_to_f32(xr[c]);
+    ss += v * v;
+  }
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) ss += __shfl_xor(ss, o);
+  if ((threadIdx.x & 63) == 0) part[threadIdx.x >> 6] = ss;
+  __syncthreads();
+  double tot = 0.0;
+#pragma unroll
+  for (int w = 0; w < kCThreads / 64; ++w) tot += part[w];
+  const double d = sqrt(tot / static_cast<double>(H) + 1e-6);
+  uint16_t* o = out + static_cast<size_t>(t) * H;
+  for (int c = threadIdx.x; c < H; c += kCThreads)
+    o[c] = f64_to_bf16(static_cast<double>(bf16_to_f32(xr[c])) / d);
+}
+
+// x = bf16(x + y): the sum is exact in double, rounded once
+__global__ __launch_bounds__(kCThreads) void residual_kernel(uint16_t* __restrict__ x,
+                                                             const float* __restrict__ y,
+                                                             size_t n) {
+  for (size_t i = static_cast<size_t>(blockIdx.x) * kCThreads + threadIdx.x; i < n;
+       i += static_cast<size_t>(gridDim.x) * kCThreads)
+    x[i] = f64_to_bf16(static_cast<double>(bf16_to_f32(x[i])) + static_cast<double>(y[i]));
+}
+
+}  // namespace
+
+hipError_t launch_combine(const float* rows, const int32_t* inv, int T, int k, int H, void* y,
+                          int y_f32, hipStream_t stream) {
+  if (T <= 0) return hipSuccess;
+  hipLaunchKernelGGL(combine_kernel, dim3(T), dim3(kCThreads), 0, stream, rows, inv, k, H, y,
+                     y_f32);
+  return hipGetLastError();
+}
+
+hipError_t launch_prenorm(const uint16_t* x, int T, int H, uint16_t* out, hipStream_t stream) {
+  if (T <= 0) return hipSuccess;
+  hipLaunchKernelGGL(prenorm_kernel, dim3(T), dim3(kCThreads), 0, stream, x, H, out);
+  return hipGetLastError();
+}
+
+hipError_t launch_residual(uint16_t* x, const float* y, int T, int H, hipStream_t stream) {
+  const size_t n = static_cast<size_t>(T) * H;
+  if (n == 0) return hipSuccess;
+  size_t g = (n + kCThreads - 1) / kCThreads;
+  if (g > 8192) g = 8192;
+  hipLaunchKernelGGL(residual_kernel, dim3(static_cast<unsigned>(g)), dim3(kCThreads), 0, stream,
+                     x, y, n);
+  return hipGetLastError();
+}
+
+}  // namespace moe

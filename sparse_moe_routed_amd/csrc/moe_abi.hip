@@ -1,0 +1,361 @@
+// C ABI of libmoe: host-side validation, workspace layout and the launch
+// sequence of the routed MoE layer.  Declarations and argument contracts are
+// in include/moe.h.
+#include <stdint.h>
+#include <string.h>
+
+#include <limits>
+
+#include "../../include/moe.h"
+#include "moe_internal.h"
+
+namespace {
+
+using moe::kBF16;
+using moe::kFP8;
+using moe::kNVFP4;
+
+constexpr int32_t kMaxTokens = 1 << 20;
+constexpr size_t kAlign = 256;
+constexpr int kTileRowsMin = 32;  // smallest rows-per-tile of any GEMM shape
+
+// MOE_EINVAL for malformed dims (null, non-positive, k > E), MOE_EUNSUPPORTED
+// for well-formed shapes outside what the kernels cover.
+moe_status dims_check(const moe_dims* d) {
+  if (!d) return MOE_EINVAL;
+  if (d->hidden <= 0 || d->ffn <= 0 || d->n_experts <= 0 || d->top_k <= 0) return MOE_EINVAL;
+  if (d->top_k > d->n_experts) return MOE_EINVAL;
+  if (d->hidden % 64 || d->ffn % 64) return MOE_EUNSUPPORTED;
+  if (d->n_experts < 16 || d->n_experts > 256 || d->n_experts % 16) return MOE_EUNSUPPORTED;
+  if (d->top_k > 8) return MOE_EUNSUPPORTED;
+  return MOE_OK;
+}
+
+bool dims_ok(const moe_dims* d) { return dims_check(d) == MOE_OK; }
+
+bool fmt_ok(int32_t fmt) { return fmt == kBF16 || fmt == kFP8 || fmt == kNVFP4; }
+
+struct Layout {
+  size_t counts, offsets, ctrl, scales, chunk_counts, chunk_base, tiles0, tiles1, sorted_src,
+      inv, row_gate, act, out_rows, x_q, act_q, total;
+  bool has_xq, has_actq, actq_inplace;
+  int max_tiles;
+};
+
+// ctrl words: [0] n_tiles0, [1] n_tiles1; scales floats: [0] x scale, [1] act scale,
+// [2] amax(x) bits, [3] amax(act) bits
+Layout make_layout(const moe_dims* d, int32_t fmt, int32_t T) {
+  Layout L{};
+  const size_t E = static_cast<size_t>(d->n_experts);
+  const size_t R = static_cast<size_t>(T) * d->top_k;
+  const size_t H = static_cast<size_t>(d->hidden), F = static_cast<size_t>(d->ffn);
+  const size_t n_chunks = R ? (R + moe::kChunk - 1) / moe::kChunk : 1;
+  const size_t max_tiles = (R + kTileRowsMin - 1) / kTileRowsMin + (R < E ? R : E) + 1;
+  size_t off = 0;
+  auto alloc = [&](size_t bytes) {
+    off = (off + kAlign - 1) / kAlign * kAlign;
+    const size_t at = off;
+    off += bytes;
+    return at;
+  };
+  L.counts = alloc(E * 4);
+  L.offsets = alloc((E + 1) * 4);
+  L.ctrl = alloc(16 * 4);
+  L.scales = alloc(16 * 4);
+  L.chunk_counts = alloc(n_chunks * E * 4);
+  L.chunk_base = alloc(n_chunks * E * 4);
+  L.tiles0 = alloc(max_tiles * 8);
+  L.tiles1 = alloc(max_tiles * 8);
+  L.sorted_src = alloc(R * 4);
+  L.inv = alloc(R * 4);
+  L.row_gate = alloc(R * 4);
+  L.act = alloc(R * F * 2);
+  L.out_rows = alloc(R * H * 4);
+  L.has_xq = fmt != kBF16;
+  L.has_actq = fmt != kBF16;
+  L.actq_inplace = fmt == kNVFP4;
+  L.x_q = L.has_xq ? alloc(static_cast<size_t>(T) * H * (fmt == kFP8 ? 1 : 2)) : 0;
+  L.act_q = fmt == kFP8 ? alloc(R * F) : L.act;
+  L.total = (off + kAlign - 1) / kAlign * kAlign;
+  L.max_tiles = static_cast<int>(max_tiles);
+  return L;
+}
+
+template <typename T>
+T* at(void* ws, size_t off) {
+  return reinterpret_cast<T*>(static_cast<uint8_t*>(ws) + off);
+}
+
+moe_status hip_status(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_EHIP; }
+
+}  // namespace
+
+extern "C" {
+
+int32_t moe_abi_version(void) { return MOE_ABI_VERSION; }
+
+const char* moe_status_str(int32_t s) {
+  switch (s) {
+    case MOE_OK: return "ok";
+    case MOE_EINVAL: return "invalid argument";
+    case MOE_EUNSUPPORTED: return "unsupported shape or format";
+    case MOE_EWORKSPACE: return "workspace missing or too small";
+    case MOE_EHIP: return "HIP launch or runtime error";
+    default: return "unknown status";
+  }
+}
+
+size_t moe_workspace_size(const moe_dims* dims, int32_t fmt, int32_t max_tokens) {
+  if (!dims_ok(dims) || !fmt_ok(fmt) || max_tokens < 0 || max_tokens > kMaxTokens) return 0;
+  return make_layout(dims, fmt, max_tokens).total;
+}
+
+int32_t moe_workspace_layout(const moe_dims* dims, int32_t fmt, int32_t T, moe_ws_layout* out) {
+  if (!out || !dims_ok(dims) || !fmt_ok(fmt) || T < 0 || T > kMaxTokens) return MOE_EINVAL;
+  const Layout L = make_layout(dims, fmt, T);
+  out->counts = static_cast<int64_t>(L.counts);
+  out->offsets = static_cast<int64_t>(L.offsets);
+  out->sorted_src = static_cast<int64_t>(L.sorted_src);
+  out->inv = static_cast<int64_t>(L.inv);
+  out->act = static_cast<int64_t>(L.act);
+  out->out_rows = static_cast<int64_t>(L.out_rows);
+  out->x_q = L.has_xq ? static_cast<int64_t>(L.x_q) : -1;
+  out->act_q = L.has_actq ? static_cast<int64_t>(L.act_q) : -1;
+  out->scales = static_cast<int64_t>(L.scales);
+  out->total = static_cast<int64_t>(L.total);
+  return MOE_OK;
+}
+
+int32_t moe_route(const moe_dims* dims, int32_t T, const void* x, const moe_router* router,
+                  int32_t* ids, float* gates, void* stream) {
+  if (const moe_status ds = dims_check(dims)) return ds;
+  if (T < 0 || T > kMaxTokens) return MOE_EINVAL;
+  if (T == 0) return MOE_OK;  // nothing is read or written; pointers may be null
+  if (!router || !router->w || !x || !ids || !gates) return MOE_EINVAL;
+  return hip_status(moe::launch_router(static_cast<const uint16_t*>(x), router->w, router->bias,
+                                       T, dims->hidden, dims->n_experts, dims->top_k, ids,
+                                       gates, static_cast<hipStream_t>(stream)));
+}
+
+}  // extern "C"
+
+namespace {
+
+// records events[stage] (if given) on the stream before each stage
+struct StageMarks {
+  void* const* ev;
+  int n;
+  hipStream_t st;
+  void mark(int i) const {
+    if (ev && i < n && ev[i]) (void)hipEventRecord(static_cast<hipEvent_t>(ev[i]), st);
+  }
+};
+
+int32_t forward_impl(const moe_dims* dims, int32_t T, const void* x, const int32_t* ids,
+                     const float* gates, const moe_experts* ex, void* y, int32_t y_dtype,
+                     void* ws, size_t ws_bytes, void* stream, void* const* events,
+                     int32_t n_events) {
+  if (const moe_status ds = dims_check(dims)) return ds;
+  if (!ex) return MOE_EINVAL;
+  if (T < 0 || T > kMaxTokens) return MOE_EINVAL;
+  if (!fmt_ok(ex->fmt)) return MOE_EINVAL;
+  if (y_dtype != MOE_Y_BF16 && y_dtype != MOE_Y_F32) return MOE_EINVAL;
+  if (T == 0) return MOE_OK;  // nothing is read or written; pointers may be null
+  if (!x || !ids || !gates || !y || !ex->up || !ex->down) return MOE_EINVAL;
+  if (ex->fmt != kBF16 && (!ex->up_s || !ex->down_s)) return MOE_EINVAL;
+  if (ex->fmt == kNVFP4 && (!ex->up_bs || !ex->down_bs)) return MOE_EINVAL;
+  const Layout L = make_layout(dims, ex->fmt, T);
+  if (!ws || ws_bytes < L.total) return MOE_EWORKSPACE;
+  if (reinterpret_cast<uintptr_t>(ws) % kAlign) return MOE_EWORKSPACE;
+
+  const hipStream_t st = static_cast<hipStream_t>(stream);
+  const StageMarks marks{events, n_events, st};
+  const int fmt = ex->fmt;
+  const int H = dims->hidden, F = dims->ffn, E = dims->n_experts, k = dims->top_k;
+  const int R = T * k;
+  int32_t* ctrl = at<int32_t>(ws, L.ctrl);
+  float* scales = at<float>(ws, L.scales);
+  uint32_t* amax_x = reinterpret_cast<uint32_t*>(scales + 2);
+  uint32_t* amax_a = reinterpret_cast<uint32_t*>(scales + 3);
+  int32_t* offsets = at<int32_t>(ws, L.offsets);
+
+  // 1. histogram, prefix sum + tile lists, stable scatter
+  moe::PermBufs p{};
+  p.chunk_counts = at<int32_t>(ws, L.chunk_counts);
+  p.chunk_base = at<int32_t>(ws, L.chunk_base);
+  p.counts = at<int32_t>(ws, L.counts);
+  p.offsets = offsets;
+  p.sorted_src = at<int32_t>(ws, L.sorted_src);
+  p.inv = at<int32_t>(ws, L.inv);
+  p.row_gate = at<float>(ws, L.row_gate);
+  p.bm0 = moe::gemm_shape(fmt, 0, T).bm;
+  p.tiles0 = at<int2>(ws, L.tiles0);
+  p.n_tiles0 = ctrl + 0;
+  p.bm1 = moe::gemm_shape(fmt, 1, T).bm;
+  p.tiles1 = at<int2>(ws, L.tiles1);
+  p.n_tiles1 = ctrl + 1;
+  p.zero_words = amax_x;  // amax(x), amax(act)
+  p.n_zero = 2;
+  marks.mark(0);
+  hipError_t err = moe::launch_permute(ids, gates, T, E, k, p, st);
+  if (err != hipSuccess) return MOE_EHIP;
+
+  // 2. token quantisation (fp8 / nvfp4)
+  marks.mark(1);
+  const void* a_up = x;
+  if (fmt == kFP8) {
+    err = moe::launch_amax_bf16(static_cast<const uint16_t*>(x), nullptr, T, H, amax_x, st);
+    if (err == hipSuccess)
+      err = moe::launch_quant_fp8(static_cast<const uint16_t*>(x), nullptr, T, H, amax_x,
+                                  at<uint8_t>(ws, L.x_q), scales + 0, st);
+    a_up = at<uint8_t>(ws, L.x_q);
+  } else if (fmt == kNVFP4) {
+    err = moe::launch_amax_bf16(static_cast<const uint16_t*>(x), nullptr, T, H, amax_x, st);
+    if (err == hipSuccess)
+      err = moe::launch_quant_nvfp4(static_cast<const uint16_t*>(x), nullptr, T, H, amax_x, 0,
+                                    at<uint16_t>(ws, L.x_q), nullptr, nullptr, scales + 0, st);
+    a_up = at<uint16_t>(ws, L.x_q);
+  }
+  if (err != hipSuccess) return MOE_EHIP;
+
+  // 3. grouped up projection + ReLU^2
+  marks.mark(2);
+  moe::GemmArgs g{};
+  g.tiles = p.tiles0;
+  g.n_tiles = p.n_tiles0;
+  g.max_tiles = (R + p.bm0 - 1) / p.bm0 + (R < E ? R : E);
+  g.offsets = offsets;
+  g.sorted_src = p.sorted_src;
+  g.top_k = k;
+  g.a = a_up;
+  g.b = ex->up;
+  g.b_bs = ex->up_bs;
+  g.b_s = ex->up_s;
+  g.a_s = scales + 0;
+  g.N = F;
+  g.K = H;
+  g.out = at<uint16_t>(ws, L.act);
+  g.row_gate = nullptr;
+  g.amax = amax_a;
+  err = moe::launch_gemm(fmt, 0, T, g, st);
+  if (err != hipSuccess) return MOE_EHIP;
+
+  // 4. intermediate quantisation (fp8 / nvfp4), rows [0, offsets[E])
+  marks.mark(3);
+  const void* a_down = at<uint16_t>(ws, L.act);
+  if (fmt == kFP8) {
+    err = moe::launch_quant_fp8(at<uint16_t>(ws, L.act), offsets + E, R, F, amax_a,
+                                at<uint8_t>(ws, L.act_q), scales + 1, st);
+    a_down = at<uint8_t>(ws, L.act_q);
+  } else if (fmt == kNVFP4) {
+    err = moe::launch_quant_nvfp4(at<uint16_t>(ws, L.act), offsets + E, R, F, amax_a, 0,
+                                  at<uint16_t>(ws, L.act), nullptr, nullptr, scales + 1, st);
+  }
+  if (err != hipSuccess) return MOE_EHIP;
+
+  // 5. grouped down projection, gate applied per row
+  marks.mark(4);
+  g.tiles = p.tiles1;
+  g.n_tiles = p.n_tiles1;
+  g.max_tiles = (R + p.bm1 - 1) / p.bm1 + (R < E ? R : E);
+  g.sorted_src = nullptr;
+  g.a = a_down;
+  g.b = ex->down;
+  g.b_bs = ex->down_bs;
+  g.b_s = ex->down_s;
+  g.a_s = scales + 1;
+  g.N = H;
+  g.K = F;
+  g.out = at<float>(ws, L.out_rows);
+  g.row_gate = p.row_gate;
+  g.amax = nullptr;
+  err = moe::launch_gemm(fmt, 1, T, g, st);
+  if (err != hipSuccess) return MOE_EHIP;
+
+  // 6. combine
+  marks.mark(5);
+  err = moe::launch_combine(at<float>(ws, L.out_rows), p.inv, T, k, H, y, y_dtype == MOE_Y_F32,
+                            st);
+  marks.mark(6);
+  return hip_status(err);
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t moe_forward(const moe_dims* dims, int32_t T, const void* x, const int32_t* ids,
+                    const float* gates, const moe_experts* ex, void* y, int32_t y_dtype,
+                    void* ws, size_t ws_bytes, void* stream) {
+  return forward_impl(dims, T, x, ids, gates, ex, y, y_dtype, ws, ws_bytes, stream, nullptr, 0);
+}
+
+int32_t moe_forward_timed(const moe_dims* dims, int32_t T, const void* x, const int32_t* ids,
+                          const float* gates, const moe_experts* ex, void* y, int32_t y_dtype,
+                          void* ws, size_t ws_bytes, void* stream, void* const* events,
+                          int32_t n_events) {
+  if (!events || n_events < MOE_N_STAGES + 1) return MOE_EINVAL;
+  return forward_impl(dims, T, x, ids, gates, ex, y, y_dtype, ws, ws_bytes, stream, events,
+                      n_events);
+}
+
+int32_t moe_quantize_experts(const moe_dims* dims, int32_t fmt, const void* up_bf16,
+                             const void* down_bf16, void* up_q, void* down_q, uint8_t* up_bs,
+                             uint8_t* down_bs, float* up_s, float* down_s, void* stream) {
+  if (const moe_status ds = dims_check(dims)) return ds;
+  if (fmt != kFP8 && fmt != kNVFP4) return MOE_EINVAL;
+  if (!up_bf16 || !down_bf16 || !up_q || !down_q || !up_s || !down_s) return MOE_EINVAL;
+  if (fmt == kNVFP4 && (!up_bs || !down_bs)) return MOE_EINVAL;
+  const hipStream_t st = static_cast<hipStream_t>(stream);
+  const int H = dims->hidden, F = dims->ffn, E = dims->n_experts;
+  hipError_t err = moe::launch_quant_weights(fmt, static_cast<const uint16_t*>(up_bf16), E, F, H,
+                                             static_cast<uint8_t*>(up_q), up_bs, up_s, st);
+  if (err == hipSuccess)
+    err = moe::launch_quant_weights(fmt, static_cast<const uint16_t*>(down_bf16), E, H, F,
+                                    static_cast<uint8_t*>(down_q), down_bs, down_s, st);
+  return hip_status(err);
+}
+
+int32_t moe_quantize_activation(int32_t fmt, int32_t rows, int32_t cols, const void* x,
+                                void* codes, uint8_t* bs, float* scale, void* ws,
+                                size_t ws_bytes, void* stream) {
+  if (fmt != kFP8 && fmt != kNVFP4) return MOE_EINVAL;
+  if (rows < 0 || cols <= 0 || cols % 64) return MOE_EINVAL;
+  if (static_cast<long long>(rows) * cols > (1ll << 31)) return MOE_EUNSUPPORTED;
+  if (!x || !codes || !scale || (fmt == kNVFP4 && !bs)) return MOE_EINVAL;
+  if (!ws || ws_bytes < kAlign) return MOE_EWORKSPACE;
+  if (rows == 0) return MOE_OK;
+  const hipStream_t st = static_cast<hipStream_t>(stream);
+  uint32_t* amax = static_cast<uint32_t*>(ws);
+  hipError_t err = moe::launch_zero_u32(amax, 1, st);
+  if (err == hipSuccess)
+    err = moe::launch_amax_bf16(static_cast<const uint16_t*>(x), nullptr, rows, cols, amax, st);
+  if (err == hipSuccess) {
+    if (fmt == kFP8)
+      err = moe::launch_quant_fp8(static_cast<const uint16_t*>(x), nullptr, rows, cols, amax,
+                                  static_cast<uint8_t*>(codes), scale, st);
+    else
+      err = moe::launch_quant_nvfp4(static_cast<const uint16_t*>(x), nullptr, rows, cols, amax, 1,
+                                    nullptr, static_cast<uint8_t*>(codes), bs, scale, st);
+  }
+  return hip_status(err);
+}
+
+int32_t moe_prenorm(int32_t T, int32_t H, const void* x, void* out, void* stream) {
+  if (T < 0 || T > kMaxTokens || H <= 0 || H % 64) return MOE_EINVAL;
+  if (!x || !out) return MOE_EINVAL;
+  if (T == 0) return MOE_OK;
+  return hip_status(moe::launch_prenorm(static_cast<const uint16_t*>(x), T, H,
+                                        static_cast<uint16_t*>(out),
+                                        static_cast<hipStream_t>(stream)));
+}
+
+int32_t moe_residual_add(int32_t T, int32_t H, void* x, const float* y, void* stream) {
+  if (T < 0 || T > kMaxTokens || H <= 0 || H % 64) return MOE_EINVAL;
+  if (!x || !y) return MOE_EINVAL;
+  if (T == 0) return MOE_OK;
+  return hip_status(moe::launch_residual(static_cast<uint16_t*>(x), y, T, H,
+                                         static_cast<hipStream_t>(stream)));
+}
+
+}  // extern "C"

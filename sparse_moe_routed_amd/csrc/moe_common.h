@@ -1,0 +1,118 @@
+// Device-side helpers shared by the libmoe kernels (gfx950 / CDNA4 only).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace moe {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef int32_t i32x8 __attribute__((ext_vector_type(8)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kWave = 64;
+
+// ----------------------------------------------------------------- bf16
+__device__ __forceinline__ float bf16_to_f32(uint16_t b) {
+  return __uint_as_float(static_cast<uint32_t>(b) << 16);
+}
+
+// round to nearest, ties to even (finite inputs; NaN maps to a quiet NaN)
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return 0x7fc0;
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return static_cast<uint16_t>(u >> 16);
+}
+
+// round a binary64 value directly to bf16 (nearest, ties to even), so that a
+// value computed exactly in double is rounded once.  Values below the bf16
+// normal range go through fp32 (they do not occur on the layer's data).
+__device__ __forceinline__ uint16_t f64_to_bf16(double d) {
+  const uint64_t u = static_cast<uint64_t>(__double_as_longlong(d));
+  const uint32_t sign = static_cast<uint32_t>(u >> 48) & 0x8000u;
+  const int e = static_cast<int>((u >> 52) & 0x7ffu) - 1023;
+  if (e < -126) return f32_to_bf16(static_cast<float>(d));
+  if (e > 127) return static_cast<uint16_t>(sign | 0x7f80u);
+  const uint64_t mant = u & 0xfffffffffffffull;
+  const uint32_t keep = static_cast<uint32_t>(mant >> 45);
+  const uint64_t rest = mant & ((1ull << 45) - 1);
+  uint32_t bits = (static_cast<uint32_t>(e + 127) << 7) | keep;
+  if (rest > (1ull << 44) || (rest == (1ull << 44) && (keep & 1u))) ++bits;  // carries into the exponent
+  return static_cast<uint16_t>(sign | bits);
+}
+
+// ----------------------------------------------------------------- E4M3 (OCP E4M3FN)
+// 1 sign, 4 exponent bits (bias 7), 3 mantissa bits, largest finite 448,
+// subnormals m * 2^-9.  Encode: nearest-even, finite inputs saturate to 448,
+// sign bit set iff v < 0.
+__device__ __forceinline__ uint32_t e4m3_encode(float v) {
+  const uint32_t sign = v < 0.f ? 0x80u : 0u;
+  const float a = fminf(fabsf(v), 448.f);
+  if (a < 0.015625f) {  // below the smallest normal 2^-6: quantum 2^-9
+    return sign | static_cast<uint32_t>(rintf(a * 512.f));  // 0..8 (8 == 2^-6)
+  }
+  const uint32_t b = __float_as_uint(a);
+  int e = static_cast<int>(b >> 23) - 127;  // -6..8
+  uint32_t keep = (b >> 20) & 7u;
+  const uint32_t rest = b & 0xfffffu;
+  if (rest > 0x80000u || (rest == 0x80000u && (keep & 1u))) ++keep;
+  if (keep == 8u) { keep = 0u; ++e; }
+  return sign | (static_cast<uint32_t>(e + 7) << 3) | keep;
+}
+
+__device__ __forceinline__ float e4m3_decode(uint32_t c) {
+  const uint32_t e = (c >> 3) & 15u, m = c & 7u;
+  float v;
+  if (e == 0u) {
+    v = static_cast<float>(m) * 0.001953125f;  // m * 2^-9
+  } else {
+    v = __uint_as_float(((e + 120u) << 23) | (m << 20));  // (1 + m/8) 2^(e-7)
+  }
+  return (c & 0x80u) ? -v : v;
+}
+
+// ----------------------------------------------------------------- E2M1 (OCP FP4)
+// 1 sign, 2 exponent bits (bias 1), 1 mantissa bit: {0, .5, 1, 1.5, 2, 3, 4, 6}.
+__device__ __forceinline__ uint32_t e2m1_encode(float v) {
+  const uint32_t sign = v < 0.f ? 8u : 0u;
+  const float a = fminf(fabsf(v), 6.f);
+  if (a < 1.f) return sign | static_cast<uint32_t>(rintf(a * 2.f));  // 0, 1, 2(=1.0)
+  const uint32_t b = __float_as_uint(a);
+  int e = static_cast<int>(b >> 23) - 127;  // 0..2
+  uint32_t keep = (b >> 22) & 1u;
+  const uint32_t rest = b & 0x3fffffu;
+  if (rest > 0x200000u || (rest == 0x200000u && (keep & 1u))) ++keep;
+  if (keep == 2u) { keep = 0u; ++e; }
+  return sign | (static_cast<uint32_t>(e + 1) << 1) | keep;
+}
+
+__device__ __forceinline__ float e2m1_decode(uint32_t c) {
+  // magnitudes by code: 0 .5 1 1.5 2 3 4 6
+  const uint32_t m = c & 7u;
+  const float mag = (m < 2u) ? 0.5f * static_cast<float>(m)
+                             : __uint_as_float(((((m >> 1) - 1u) + 127u) << 23) | ((m & 1u) << 22));
+  return (c & 8u) ? -mag : mag;
+}
+
+// ----------------------------------------------------------------- wave helpers
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
+  return v;
+}
+
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
+  return v;
+}
+
+// non-negative floats order like their bit patterns
+__device__ __forceinline__ void atomic_max_nonneg(uint32_t* slot, float v) {
+  atomicMax(slot, __float_as_uint(v));
+}
+
+}  // namespace moe

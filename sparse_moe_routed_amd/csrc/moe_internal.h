@@ -1,0 +1,92 @@
+// Internal launchers of libmoe (host side).  Not part of the C ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace moe {
+
+enum Fmt { kBF16 = 0, kFP8 = 1, kNVFP4 = 2 };
+
+constexpr int kChunk = 2048;  // flat (token, slot) entries per permutation chunk
+
+struct PermBufs {
+  int32_t* chunk_counts;  // [n_chunks, E]
+  int32_t* chunk_base;    // [n_chunks, E]
+  int32_t* counts;        // [E]
+  int32_t* offsets;       // [E + 1]
+  int32_t* sorted_src;    // [R]
+  int32_t* inv;           // [R]
+  float* row_gate;        // [R]
+  int bm0;                // rows per tile, list 0 (up projection)
+  int2* tiles0;
+  int32_t* n_tiles0;
+  int bm1;                // rows per tile, list 1 (down projection)
+  int2* tiles1;
+  int32_t* n_tiles1;
+  uint32_t* zero_words;   // cleared by the scan (amax slots)
+  int n_zero;
+};
+
+hipError_t launch_router(const uint16_t* x, const float* w, const float* bias, int T, int H,
+                         int E, int k, int32_t* ids, float* gates, hipStream_t stream);
+
+hipError_t launch_permute(const int32_t* ids, const float* gates, int T, int E, int k,
+                          const PermBufs& p, hipStream_t stream);
+
+// Grouped GEMM over the tile list.  Up: out = bf16(relu(scale * A_g W^T)^2)
+// with A_g the token rows gathered through sorted_src; down:
+// out = fp32(gate * scale * A W^T).
+struct GemmArgs {
+  const int2* tiles;
+  const int32_t* n_tiles;
+  int max_tiles;
+  const int32_t* offsets;     // [E + 1]
+  const int32_t* sorted_src;  // up only: flat index of each sorted row
+  int top_k;
+  const void* a;              // up: tokens [T, K]; down: activations [R, K]
+  const void* b;              // expert weights, [E, N, K] (packed K/2 for nvfp4)
+  const uint8_t* b_bs;        // nvfp4 block scales [E, N, K/16]
+  const float* b_s;           // fp8 / nvfp4 weight scale per expert [E]
+  const float* a_s;           // fp8 / nvfp4 activation scale (device scalar)
+  int N, K;
+  void* out;                  // up: bf16 [R, N]; down: fp32 [R, N]
+  const float* row_gate;      // down only: [R]
+  uint32_t* amax;             // up with fp8 / nvfp4: amax of the bf16 output
+};
+
+struct GemmShape {
+  int bm, bn;
+};
+
+// Tile shape the forward pass uses for T tokens (rows per tile feeds the
+// permutation's tile lists).
+GemmShape gemm_shape(int fmt, int stage, int T);
+
+hipError_t launch_gemm(int fmt, int stage, int T, const GemmArgs& g, hipStream_t stream);
+
+// activation quantisers
+hipError_t launch_amax_bf16(const uint16_t* x, const int32_t* n_rows_dev, int rows, int cols,
+                            uint32_t* amax, hipStream_t stream);
+// FP8: codes = E4M3(f32(x * f32(448/amax))); writes scale f32(amax/448) to *scale
+hipError_t launch_quant_fp8(const uint16_t* x, const int32_t* n_rows_dev, int rows, int cols,
+                            const uint32_t* amax, uint8_t* codes, float* scale,
+                            hipStream_t stream);
+// NVFP4: per 16-block codes and E4M3 scale; writes tensor scale to *scale.
+// mode 0: dequantised block values dec(q)*dec(sb) as bf16 into deq (may alias x);
+// mode 1: packed codes + block scales.
+hipError_t launch_quant_nvfp4(const uint16_t* x, const int32_t* n_rows_dev, int rows, int cols,
+                              const uint32_t* amax, int mode, uint16_t* deq, uint8_t* codes,
+                              uint8_t* bs, float* scale, hipStream_t stream);
+hipError_t launch_zero_u32(uint32_t* p, int n, hipStream_t stream);
+
+hipError_t launch_combine(const float* rows, const int32_t* inv, int T, int k, int H, void* y,
+                          int y_f32, hipStream_t stream);
+
+hipError_t launch_quant_weights(int fmt, const uint16_t* w, int E, int N, int K, uint8_t* q,
+                                uint8_t* bs, float* s, hipStream_t stream);
+
+hipError_t launch_prenorm(const uint16_t* x, int T, int H, uint16_t* out, hipStream_t stream);
+hipError_t launch_residual(uint16_t* x, const float* y, int T, int H, hipStream_t stream);
+
+}  // namespace moe

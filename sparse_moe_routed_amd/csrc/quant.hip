@@ -1,0 +1,307 @@
+// Per-tensor quantisers for the FP8 (scalar-scale E4M3, W8A8) and 4-bit
+// (NVFP4, W4A4) expert formats (bloomery issue #967, section 2 "Checkpoint
+// facts"; section 6 keeps each release's W8A8/W4A4 activation rules).
+//
+// Recipes, each step an IEEE float32 operation:
+//   FP8   s = amax / 448,  inv = 448 / amax,  code = E4M3(v * inv)
+//   NVFP4 S = amax / 2688 (= 6 * 448),  per 16-element block along K:
+//         sb = E4M3(amax_b / (6 * S)); sb == 0 -> zero block;
+//         r = 1 / (dec(sb) * S),  code = E2M1(v * r)
+//   amax == 0 -> zero codes and a zero scale.
+// The same kernels pack expert weights (one scale per expert projection) and
+// quantise activations inside the forward pass (one scale per tensor).
+#include "moe_common.h"
+#include "moe_internal.h"
+
+namespace moe {
+
+namespace {
+
+constexpr int kQThreads = 256;
+
+__device__ __forceinline__ uint32_t load_amax_bits(const uint32_t* p) {
+  return __atomic_load_n(p, __ATOMIC_RELAXED);
+}
+
+__global__ __launch_bounds__(kQThreads) void zero_u32_kernel(uint32_t* p, int n) {
+  const int i = blockIdx.x * kQThreads + threadIdx.x;
+  if (i < n) p[i] = 0u;
+}
+
+// amax over rows [0, n_rows) of a bf16 [rows, cols] tensor; 8 elements per thread step
+__global__ __launch_bounds__(kQThreads) void amax_bf16_kernel(const uint16_t* __restrict__ x,
+                                                              const int32_t* n_rows_dev, int rows,
+                                                              int cols, uint32_t* amax) {
+  const int nr = n_rows_dev ? min(*n_rows_dev, rows) : rows;
+  const size_t n8 = static_cast<size_t>(nr) * cols / 8;
+  float m = 0.f;
+  for (size_t i = static_cast<size_t>(blockIdx.x) * kQThreads + threadIdx.x; i < n8;
+       i += static_cast<size_t>(gridDim.x) * kQThreads) {
+    const u32x4 v = reinterpret_cast<const u32x4*>(x)[i];
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      m = fmaxf(m, fabsf(bf16_to_f32(v[w] & 0xffffu)));
+      m = fmaxf(m, fabsf(bf16_to_f32(v[w] >> 16)));
+    }
+  }
+  m = wave_max(m);
+  if ((threadIdx.x & 63) == 0) atomic_max_nonneg(amax, m);
+}
+
+// FP8: 16 elements per thread
+__global__ __launch_bounds__(kQThreads) void quant_fp8_kernel(const uint16_t* __restrict__ x,
+                                                              const int32_t* n_rows_dev, int rows,
+                                                              int cols, const uint32_t* amax_p,
+                                                              uint8_t* __restrict__ codes,
+                                                              float* scale) {
+  const float amax = __uint_as_float(load_amax_bits(amax_p));
+  if (blockIdx.x == 0 && threadIdx.x == 0) *scale = amax > 0.f ? __fdiv_rn(amax, 448.f) : 0.f;
+  const int nr = n_rows_dev ? min(*n_rows_dev, rows) : rows;
+  const size_t n16 = static_cast<size_t>(nr) * cols / 16;
+  const float inv = amax > 0.f ? __fdiv_rn(448.f, amax) : 0.f;
+  for (size_t i = static_cast<size_t>(blockIdx.x) * kQThreads + threadIdx.x; i < n16;
+       i += static_cast<size_t>(gridDim.x) * kQThreads) {
+    const u32x4 v0 = reinterpret_cast<const u32x4*>(x)[2 * i];
+    const u32x4 v1 = reinterpret_cast<const u32x4*>(x)[2 * i + 1];
+    uint32_t out[4];
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      const uint32_t a = w < 2 ? v0[2 * w] : v1[2 * (w - 2)];
+      const uint32_t b = w < 2 ? v0[2 * w + 1] : v1[2 * (w - 2) + 1];
+      uint32_t q0 = 0, q1 = 0, q2 = 0, q3 = 0;
+      if (amax > 0.f) {
+        q0 = e4m3_encode(bf16_to_f32(a & 0xffffu) * inv);
+        q1 = e4m3_encode(bf16_to_f32(a >> 16) * inv);
+        q2 = e4m3_encode(bf16_to_f32(b & 0xffffu) * inv);
+        q3 = e4m3_encode(bf16_to_f32(b >> 16) * inv);
+      }
+      out[w] = q0 | (q1 << 8) | (q2 << 16) | (q3 << 24);
+    }
+    reinterpret_cast<u32x4*>(codes)[i] = u32x4{out[0], out[1], out[2], out[3]};
+  }
+}
+
+// NVFP4: one 16-element block per thread.  mode 0 writes the bf16 values
+// dec(q) * dec(sb) (exact in bf16) into deq, which may alias x; mode 1 writes
+// packed codes and block scale codes.
+__global__ __launch_bounds__(kQThreads) void quant_nvfp4_kernel(
+    const uint16_t* x, const int32_t* n_rows_dev, int rows, int cols, const uint32_t* amax_p,
+    int mode, uint16_t* deq, uint8_t* __restrict__ codes, uint8_t* __restrict__ bs,
+    float* scale) {
+  const float amax = __uint_as_float(load_amax_bits(amax_p));
+  const float S = amax > 0.f ? __fdiv_rn(amax, 2688.f) : 0.f;
+  if (blockIdx.x == 0 && threadIdx.x == 0 && scale) *scale = S;
+  const float sixS = 6.f * S;
+  const int nr = n_rows_dev ? min(*n_rows_dev, rows) : rows;
+  const size_t nblk = static_cast<size_t>(nr) * cols / 16;
+  for (size_t i = static_cast<size_t>(blockIdx.x) * kQThreads + threadIdx.x; i < nblk;
+       i += static_cast<size_t>(gridDim.x) * kQThreads) {
+    const u32x4 v0 = reinterpret_cast<const u32x4*>(x)[2 * i];
+    const u32x4 v1 = reinterpret_cast<const u32x4*>(x)[2 * i + 1];
+    float v[16];
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      v[2 * w] = bf16_to_f32(v0[w] & 0xffffu);
+      v[2 * w + 1] = bf16_to_f32(v0[w] >> 16);
+      v[8 + 2 * w] = bf16_to_f32(v1[w] & 0xffffu);
+      v[8 + 2 * w + 1] = bf16_to_f32(v1[w] >> 16);
+    }
+    float amax_b = 0.f;
+#pragma unroll
+    for (int j = 0; j < 16; ++j) amax_b = fmaxf(amax_b, fabsf(v[j]));
+    uint32_t sb = 0u;
+    float sbf = 0.f;
+    if (S > 0.f) {
+      sb = e4m3_encode(__fdiv_rn(amax_b, sixS));
+      sbf = e4m3_decode(sb);
+    }
+    uint32_t q[16];
+    if (sbf > 0.f) {
+      const float r = __fdiv_rn(1.f, sbf * S);
+#pragma unroll
+      for (int j = 0; j < 16; ++j) q[j] = e2m1_encode(v[j] * r);
+    } else {
+#pragma unroll
+      for (int j = 0; j < 16; ++j) q[j] = 0u;
+    }
+    if (mode == 0) {
+      uint32_t o[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const float d0 = e2m1_decode(q[2 * j]) * sbf;  // exact
+        const float d1 = e2m1_decode(q[2 * j + 1]) * sbf;
+        o[j] = (__float_as_uint(d0) >> 16) | (__float_as_uint(d1) & 0xffff0000u);
+      }
+      reinterpret_cast<u32x4*>(deq)[2 * i] = u32x4{o[0], o[1], o[2], o[3]};
+      reinterpret_cast<u32x4*>(deq)[2 * i + 1] = u32x4{o[4], o[5], o[6], o[7]};
+    } else {
+      uint32_t p0 = 0u, p1 = 0u;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        p0 |= (q[2 * j] | (q[2 * j + 1] << 4)) << (8 * j);
+        p1 |= (q[8 + 2 * j] | (q[8 + 2 * j + 1] << 4)) << (8 * j);
+      }
+      reinterpret_cast<uint2*>(codes)[i] = make_uint2(p0, p1);
+      bs[i] = static_cast<uint8_t>(sb);
+    }
+  }
+}
+
+// ---- expert weights: per-expert amax into s (as bits), codes, then scales
+__global__ __launch_bounds__(kQThreads) void weight_amax_kernel(const uint16_t* __restrict__ w,
+                                                                size_t per_expert,
+                                                                uint32_t* amax) {
+  const int e = blockIdx.y;
+  const uint16_t* base = w + static_cast<size_t>(e) * per_expert;
+  const size_t n8 = per_expert / 8;
+  float m = 0.f;
+  for (size_t i = static_cast<size_t>(blockIdx.x) * kQThreads + threadIdx.x; i < n8;
+       i += static_cast<size_t>(gridDim.x) * kQThreads) {
+    const u32x4 v = reinterpret_cast<const u32x4*>(base)[i];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      m = fmaxf(m, fabsf(bf16_to_f32(v[q] & 0xffffu)));
+      m = fmaxf(m, fabsf(bf16_to_f32(v[q] >> 16)));
+    }
+  }
+  m = wave_max(m);
+  if ((threadIdx.x & 63) == 0) atomic_max_nonneg(amax + e, m);
+}
+
+__global__ __launch_bounds__(kQThreads) void weight_codes_kernel(
+    int fmt, const uint16_t* __restrict__ w, size_t per_expert, const uint32_t* amax,
+    uint8_t* __restrict__ q, uint8_t* __restrict__ bs) {
+  const int e = blockIdx.y;
+  const float a = __uint_as_float(amax[e]);
+  const uint16_t* base = w + static_cast<size_t>(e) * per_expert;
+  const size_t n16 = per_expert / 16;
+  if (fmt == kFP8) {
+    const float inv = a > 0.f ? __fdiv_rn(448.f, a) : 0.f;
+    uint8_t* qe = q + static_cast<size_t>(e) * per_expert;
+    for (size_t i = static_cast<size_t>(blockIdx.x) * kQThreads + threadIdx.x; i < n16;
+         i += static_cast<size_t>(gridDim.x) * kQThreads) {
+      const u32x4 v0 = reinterpret_cast<const u32x4*>(base)[2 * i];
+      const u32x4 v1 = reinterpret_cast<const u32x4*>(base)[2 * i + 1];
+      uint32_t out[4];
+#pragma unroll
+      for (int ww = 0; ww < 4; ++ww) {
+        const uint32_t x0 = ww < 2 ? v0[2 * ww] : v1[2 * (ww - 2)];
+        const uint32_t x1 = ww < 2 ? v0[2 * ww + 1] : v1[2 * (ww - 2) + 1];
+        uint32_t c[4] = {0u, 0u, 0u, 0u};
+        if (a > 0.f) {
+          c[0] = e4m3_encode(bf16_to_f32(x0 & 0xffffu) * inv);
+          c[1] = e4m3_encode(bf16_to_f32(x0 >> 16) * inv);
+          c[2] = e4m3_encode(bf16_to_f32(x1 & 0xffffu) * inv);
+          c[3] = e4m3_encode(bf16_to_f32(x1 >> 16) * inv);
+        }
+        out[ww] = c[0] | (c[1] << 8) | (c[2] << 16) | (c[3] << 24);
+      }
+      reinterpret_cast<u32x4*>(qe)[i] = u32x4{out[0], out[1], out[2], out[3]};
+    }
+  } else {
+    const float S = a > 0.f ? __fdiv_rn(a, 2688.f) : 0.f;
+    const float sixS = 6.f * S;
+    uint8_t* qe = q + static_cast<size_t>(e) * (per_expert / 2);
+    uint8_t* be = bs + static_cast<size_t>(e) * (per_expert / 16);
+    for (size_t i = static_cast<size_t>(blockIdx.x) * kQThreads + threadIdx.x; i < n16;
+         i += static_cast<size_t>(gridDim.x) * kQThreads) {
+      const u32x4 v0 = reinterpret_cast<const u32x4*>(base)[2 * i];
+      const u32x4 v1 = reinterpret_cast<const u32x4*>(base)[2 * i + 1];
+      float v[16];
+#pragma unroll
+      for (int ww = 0; ww < 4; ++ww) {
+        v[2 * ww] = bf16_to_f32(v0[ww] & 0xffffu);
+        v[2 * ww + 1] = bf16_to_f32(v0[ww] >> 16);
+        v[8 + 2 * ww] = bf16_to_f32(v1[ww] & 0xffffu);
+        v[8 + 2 * ww + 1] = bf16_to_f32(v1[ww] >> 16);
+      }
+      float amax_b = 0.f;
+#pragma unroll
+      for (int j = 0; j < 16; ++j) amax_b = fmaxf(amax_b, fabsf(v[j]));
+      uint32_t sb = 0u;
+      float sbf = 0.f;
+      if (S > 0.f) {
+        sb = e4m3_encode(__fdiv_rn(amax_b, sixS));
+        sbf = e4m3_decode(sb);
+      }
+      uint32_t p0 = 0u, p1 = 0u;
+      if (sbf > 0.f) {
+        const float r = __fdiv_rn(1.f, sbf * S);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          p0 |= (e2m1_encode(v[2 * j] * r) | (e2m1_encode(v[2 * j + 1] * r) << 4)) << (8 * j);
+          p1 |= (e2m1_encode(v[8 + 2 * j] * r) | (e2m1_encode(v[8 + 2 * j + 1] * r) << 4))
+                << (8 * j);
+        }
+      }
+      reinterpret_cast<uint2*>(qe)[i] = make_uint2(p0, p1);
+      be[i] = static_cast<uint8_t>(sb);
+    }
+  }
+}
+
+__global__ void weight_scales_kernel(int fmt, int E, float* s) {
+  const int e = blockIdx.x * blockDim.x + threadIdx.x;
+  if (e >= E) return;
+  const float a = __uint_as_float(reinterpret_cast<uint32_t*>(s)[e]);
+  s[e] = a > 0.f ? __fdiv_rn(a, fmt == kFP8 ? 448.f : 2688.f) : 0.f;
+}
+
+int grid_for(size_t work, int cap) {
+  size_t b = (work + kQThreads - 1) / kQThreads;
+  if (b < 1) b = 1;
+  return static_cast<int>(b < static_cast<size_t>(cap) ? b : cap);
+}
+
+}  // namespace
+
+hipError_t launch_zero_u32(uint32_t* p, int n, hipStream_t stream) {
+  if (n <= 0) return hipSuccess;
+  hipLaunchKernelGGL(zero_u32_kernel, dim3((n + kQThreads - 1) / kQThreads), dim3(kQThreads), 0,
+                     stream, p, n);
+  return hipGetLastError();
+}
+
+hipError_t launch_amax_bf16(const uint16_t* x, const int32_t* n_rows_dev, int rows, int cols,
+                            uint32_t* amax, hipStream_t stream) {
+  const int grid = grid_for(static_cast<size_t>(rows) * cols / 8, 2048);
+  hipLaunchKernelGGL(amax_bf16_kernel, dim3(grid), dim3(kQThreads), 0, stream, x, n_rows_dev,
+                     rows, cols, amax);
+  return hipGetLastError();
+}
+
+hipError_t launch_quant_fp8(const uint16_t* x, const int32_t* n_rows_dev, int rows, int cols,
+                            const uint32_t* amax, uint8_t* codes, float* scale,
+                            hipStream_t stream) {
+  const int grid = grid_for(static_cast<size_t>(rows) * cols / 16, 4096);
+  hipLaunchKernelGGL(quant_fp8_kernel, dim3(grid), dim3(kQThreads), 0, stream, x, n_rows_dev,
+                     rows, cols, amax, codes, scale);
+  return hipGetLastError();
+}
+
+hipError_t launch_quant_nvfp4(const uint16_t* x, const int32_t* n_rows_dev, int rows, int cols,
+                              const uint32_t* amax, int mode, uint16_t* deq, uint8_t* codes,
+                              uint8_t* bs, float* scale, hipStream_t stream) {
+  const int grid = grid_for(static_cast<size_t>(rows) * cols / 16, 4096);
+  hipLaunchKernelGGL(quant_nvfp4_kernel, dim3(grid), dim3(kQThreads), 0, stream, x, n_rows_dev,
+                     rows, cols, amax, mode, deq, codes, bs, scale);
+  return hipGetLastError();
+}
+
+hipError_t launch_quant_weights(int fmt, const uint16_t* w, int E, int N, int K, uint8_t* q,
+                                uint8_t* bs, float* s, hipStream_t stream) {
+  const size_t per = static_cast<size_t>(N) * K;
+  hipError_t err = launch_zero_u32(reinterpret_cast<uint32_t*>(s), E, stream);
+  if (err != hipSuccess) return err;
+  const int gx = grid_for(per / 8, 64);
+  hipLaunchKernelGGL(weight_amax_kernel, dim3(gx, E), dim3(kQThreads), 0, stream, w, per,
+                     reinterpret_cast<uint32_t*>(s));
+  const int gq = grid_for(per / 16, 64);
+  hipLaunchKernelGGL(weight_codes_kernel, dim3(gq, E), dim3(kQThreads), 0, stream, fmt, w, per,
+                     reinterpret_cast<const uint32_t*>(s), q, bs);
+  hipLaunchKernelGGL(weight_scales_kernel, dim3((E + 255) / 256), dim3(256), 0, stream, fmt, E,
+                     s);
+  return hipGetLastError();
+}
+
+}  // namespace moe

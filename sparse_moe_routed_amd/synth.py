@@ -111,6 +111,11 @@ def make_tokens(T: int, dims: Dims = Dims(), outliers: bool = False) -> torch.Te
     return _to_bf16(x)
 
 
+def make_f32(shape, seed: int) -> torch.Tensor:
+    """Standard-normal fp32 tensor from rng(seed) (generic test rows)."""
+    return torch.from_numpy(np.random.default_rng(seed).standard_normal(shape, dtype=np.float32))
+
+
 # Workloads: the single-layer decode/prefill shapes and the stacked 4-bit path.
 WORKLOADS = {
     "decode_t4_bf16": dict(T=4, fmt="bf16", outliers=False, layers=1),

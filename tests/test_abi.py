@@ -1,0 +1,167 @@
+"""C-ABI checks that need no GPU: the library loads, exports what
+include/moe.h declares, and rejects bad arguments before any launch."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import sparse_moe_routed_amd as moe
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "moe.h")
+
+FAKE = ctypes.c_void_p(0x100000)  # never dereferenced: every call below fails validation first
+
+
+def header_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(moe_[a-z_]+)\s*\(", text)))
+
+
+def header_abi_version():
+    return int(re.search(r"#define\s+MOE_ABI_VERSION\s+(\d+)", open(HEADER).read()).group(1))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(moe.LIB_PATH):
+        pytest.fail("libmoe.so is not built: run `python -m sparse_moe_routed_amd.build`")
+    return moe.lib()
+
+
+def test_exports_every_declared_symbol(lib):
+    names = header_functions()
+    assert "moe_route" in names and "moe_forward" in names
+    raw = ctypes.CDLL(moe.LIB_PATH)
+    for n in names:
+        assert hasattr(raw, n), n
+    # the binding describes exactly the declared functions
+    assert sorted(moe._SIGS) == names
+
+
+def test_version_and_status_strings(lib):
+    assert moe.abi_version() == header_abi_version()
+    assert moe.status_str(moe.OK) == "ok"
+    for s in (moe.EINVAL, moe.EUNSUPPORTED, moe.EWORKSPACE, moe.EHIP, 99):
+        assert moe.status_str(s)
+
+
+def _dims(h=2688, f=1856, e=128, k=6):
+    return moe.Dims(h, f, e, k)
+
+
+def test_workspace_size(lib):
+    d = _dims()
+    sizes = [lib.moe_workspace_size(ctypes.byref(d), fmt, T)
+             for fmt in (0, 1, 2) for T in (0, 1, 4, 64, 511, 512, 4096)]
+    assert all(s > 0 and s % 256 == 0 for s in sizes)
+    for fmt in (0, 1, 2):
+        prev = 0
+        for T in range(0, 3000, 37):
+            s = lib.moe_workspace_size(ctypes.byref(d), fmt, T)
+            assert s >= prev
+            prev = s
+    assert lib.moe_workspace_size(None, 0, 4) == 0
+    assert lib.moe_workspace_size(ctypes.byref(d), 7, 4) == 0
+    assert lib.moe_workspace_size(ctypes.byref(d), 0, -1) == 0
+    assert lib.moe_workspace_size(ctypes.byref(_dims(h=100)), 0, 4) == 0
+    # fp32 rows of the down projection dominate: T*k*H*4 bytes
+    assert lib.moe_workspace_size(ctypes.byref(d), 0, 4096) > 4096 * 6 * 2688 * 4
+
+
+def test_workspace_layout(lib):
+    lay = moe.workspace_layout(moe.LayerDims(), "fp8", 64)
+    assert lay["x_q"] > 0 and lay["act_q"] > 0 and lay["total"] > lay["out_rows"]
+    lay = moe.workspace_layout(moe.LayerDims(), "bf16", 64)
+    assert lay["x_q"] == -1 and lay["act_q"] == -1
+    lay = moe.workspace_layout(moe.LayerDims(), "nvfp4", 64)
+    assert lay["act_q"] == lay["act"]  # quantised in place
+    offs = [lay[k] for k in ("counts", "offsets", "sorted_src", "inv", "act", "out_rows", "scales")]
+    assert all(o % 256 == 0 for o in offs)
+
+
+def test_route_validation(lib):
+    d = _dims()
+    r = moe.Router(FAKE.value, None)
+    st = None
+    assert lib.moe_route(None, 4, FAKE, ctypes.byref(r), FAKE, FAKE, st) == moe.EINVAL
+    assert lib.moe_route(ctypes.byref(d), -1, FAKE, ctypes.byref(r), FAKE, FAKE, st) == moe.EINVAL
+    assert lib.moe_route(ctypes.byref(d), 4, None, ctypes.byref(r), FAKE, FAKE, st) == moe.EINVAL
+    assert lib.moe_route(ctypes.byref(d), 4, FAKE, None, FAKE, FAKE, st) == moe.EINVAL
+    r0 = moe.Router(None, None)
+    assert lib.moe_route(ctypes.byref(d), 4, FAKE, ctypes.byref(r0), FAKE, FAKE, st) == moe.EINVAL
+    assert lib.moe_route(ctypes.byref(_dims(k=0)), 4, FAKE, ctypes.byref(r), FAKE, FAKE, st) == moe.EINVAL
+    assert lib.moe_route(ctypes.byref(_dims(e=8, k=9)), 4, FAKE, ctypes.byref(r), FAKE, FAKE, st) == moe.EINVAL
+    assert lib.moe_route(ctypes.byref(_dims(k=9)), 4, FAKE, ctypes.byref(r), FAKE, FAKE, st) == moe.EUNSUPPORTED
+    assert lib.moe_route(ctypes.byref(_dims(e=120)), 4, FAKE, ctypes.byref(r), FAKE, FAKE, st) == moe.EUNSUPPORTED
+    assert lib.moe_route(ctypes.byref(_dims(h=2690)), 4, FAKE, ctypes.byref(r), FAKE, FAKE, st) == moe.EUNSUPPORTED
+    # T == 0 is a no-op that touches nothing
+    assert lib.moe_route(ctypes.byref(d), 0, FAKE, ctypes.byref(r), FAKE, FAKE, st) == moe.OK
+
+
+def test_forward_validation(lib):
+    d = _dims()
+    ex = moe.Experts(0, FAKE.value, FAKE.value, None, None, None, None)
+    need = lib.moe_workspace_size(ctypes.byref(d), 0, 4)
+
+    def call(dims=d, T=4, x=FAKE, ids=FAKE, gates=FAKE, e=ex, y=FAKE, yd=1, ws=FAKE, wsb=need):
+        return lib.moe_forward(dims if dims is None else ctypes.byref(dims), T, x, ids, gates,
+                               e if e is None else ctypes.byref(e), y, yd, ws, wsb, None)
+
+    assert call(dims=None) == moe.EINVAL
+    assert call(e=None) == moe.EINVAL
+    assert call(T=-3) == moe.EINVAL
+    assert call(T=(1 << 20) + 1) == moe.EINVAL
+    assert call(x=None) == moe.EINVAL
+    assert call(ids=None) == moe.EINVAL
+    assert call(gates=None) == moe.EINVAL
+    assert call(y=None) == moe.EINVAL
+    assert call(yd=5) == moe.EINVAL
+    assert call(e=moe.Experts(9, FAKE.value, FAKE.value, None, None, None, None)) == moe.EINVAL
+    assert call(e=moe.Experts(0, None, FAKE.value, None, None, None, None)) == moe.EINVAL
+    # quantised formats need their scales (and block scales for nvfp4)
+    assert call(e=moe.Experts(1, FAKE.value, FAKE.value, None, None, None, None)) == moe.EINVAL
+    assert call(e=moe.Experts(2, FAKE.value, FAKE.value, None, None, FAKE.value, FAKE.value)) == moe.EINVAL
+    assert call(dims=_dims(f=1850)) == moe.EUNSUPPORTED
+    # workspace: missing, too small, misaligned
+    assert call(ws=None) == moe.EWORKSPACE
+    assert call(wsb=need - 1) == moe.EWORKSPACE
+    assert call(ws=ctypes.c_void_p(FAKE.value + 16)) == moe.EWORKSPACE
+    # T == 0: nothing to do, no workspace needed
+    assert call(T=0, ws=None, wsb=0) == moe.OK
+
+
+def test_quantize_validation(lib):
+    d = _dims()
+    q = lib.moe_quantize_experts
+    assert q(ctypes.byref(d), 0, FAKE, FAKE, FAKE, FAKE, None, None, FAKE, FAKE, None) == moe.EINVAL
+    assert q(ctypes.byref(d), 2, FAKE, FAKE, FAKE, FAKE, None, None, FAKE, FAKE, None) == moe.EINVAL
+    assert q(ctypes.byref(d), 1, None, FAKE, FAKE, FAKE, None, None, FAKE, FAKE, None) == moe.EINVAL
+    a = lib.moe_quantize_activation
+    assert a(0, 4, 64, FAKE, FAKE, None, FAKE, FAKE, 256, None) == moe.EINVAL
+    assert a(1, 4, 60, FAKE, FAKE, None, FAKE, FAKE, 256, None) == moe.EINVAL
+    assert a(2, 4, 64, FAKE, FAKE, None, FAKE, FAKE, 256, None) == moe.EINVAL
+    assert a(1, 4, 64, FAKE, FAKE, None, FAKE, FAKE, 16, None) == moe.EWORKSPACE
+    assert a(1, 0, 64, FAKE, FAKE, None, FAKE, FAKE, 256, None) == moe.OK
+    assert lib.moe_prenorm(4, 63, FAKE, FAKE, None) == moe.EINVAL
+    assert lib.moe_prenorm(0, 64, FAKE, FAKE, None) == moe.OK
+    assert lib.moe_residual_add(4, 64, None, FAKE, None) == moe.EINVAL
+
+
+def test_binding_fails_loudly_without_library(monkeypatch):
+    monkeypatch.setattr(moe, "_lib", None)
+    monkeypatch.setattr(moe, "LIB_PATH", os.path.join(ROOT, "no_such_libmoe.so"))
+    with pytest.raises(ImportError):
+        moe.lib()
+
+
+def test_product_path_never_touches_the_oracle():
+    pkg = os.path.join(ROOT, "sparse_moe_routed_amd")
+    for dirpath, _, files in os.walk(pkg):
+        for f in files:
+            if f.endswith((".py", ".hip", ".h", ".cpp")):
+                text = open(os.path.join(dirpath, f)).read()
+                assert not re.search(r"^\s*(from|import)\s+oracle\b", text, re.M), f
+                assert "oracle." not in text.replace("the oracle.", ""), f

@@ -1,0 +1,335 @@
+"""GPU parity: the HIP path (through the C ABI) against the CPU oracle.
+
+Tolerances (max |delta| over all elements, relative to rms of the oracle
+output): 2e-2 for BF16, 5e-2 for FP8, 1e-1 for the 4-bit format, on fp32
+output; bit-exact for expert ids (except near-ties, gap < 1e-5, which are
+counted), the permutation and every quantised code.
+"""
+import numpy as np
+import pytest
+import torch
+
+import sparse_moe_routed_amd as moe
+from oracle import codecs
+from oracle import moe as om
+from sparse_moe_routed_amd import synth
+
+pytestmark = pytest.mark.gpu
+
+TOL = {"bf16": 2e-2, "fp8": 5e-2, "nvfp4": 1e-1}
+FULL = synth.Dims()
+SMALL = synth.Dims(hidden=256, ffn=192, n_experts=32, top_k=4)
+
+
+def _ld(d: synth.Dims) -> moe.LayerDims:
+    return moe.LayerDims(d.hidden, d.ffn, d.n_experts, d.top_k)
+
+
+def _log(msg):
+    print(msg, flush=True)
+
+
+class Layer:
+    """One layer's inputs on CPU (for the oracle) and GPU (for the library)."""
+
+    def __init__(self, dims: synth.Dims, layer: int = 0):
+        self.dims = dims
+        self.w_r, self.b = synth.make_router(layer, dims)
+        self.up, self.down = synth.make_experts(layer, dims)
+        self.w_r_d = self.w_r.cuda()
+        self.b_d = self.b.cuda()
+        self.up_d = self.up.cuda()
+        self.down_d = self.down.cuda()
+        self._banks = {}
+
+    def bank(self, fmt):
+        if fmt not in self._banks:
+            self._banks[fmt] = moe.quantize_experts(self.up_d, self.down_d, fmt, _ld(self.dims))
+        return self._banks[fmt]
+
+    def oracle_bank(self, fmt):
+        return om.ExpertBank(self.up, self.down, fmt)
+
+
+@pytest.fixture(scope="module")
+def full():
+    _log("generating full-size layer 0")
+    return Layer(FULL, 0)
+
+
+@pytest.fixture(scope="module")
+def small():
+    return Layer(SMALL, 0)
+
+
+def _x(T, dims, outliers=False):
+    return synth.make_tokens(T, dims, outliers=outliers)
+
+
+def _rel_err(y_gpu, y_ref):
+    rms = np.sqrt(np.mean(y_ref ** 2))
+    return np.abs(y_gpu - y_ref).max() / rms, rms
+
+
+def _route_both(L, x):
+    ids_o, g_o, gap, _ = om.route(x.float().numpy(), L.w_r.numpy(), L.b.numpy(), L.dims.top_k)
+    ids_g, g_g = moe.route(x.cuda(), L.w_r_d, L.b_d, _ld(L.dims))
+    torch.cuda.synchronize()
+    return ids_o, g_o, gap, ids_g.cpu().numpy(), g_g.cpu().numpy()
+
+
+# --------------------------------------------------------------------------- router
+@pytest.mark.parametrize("T", [1, 4, 64, 333])
+def test_router_matches_oracle(full, T):
+    x = _x(T, FULL, outliers=T > 100)
+    ids_o, g_o, gap, ids_g, g_g = _route_both(full, x)
+    near = gap < om.NEAR_TIE
+    _log(f"T={T}: near-ties {int(near.sum())}, min gap {gap.min():.2e}")
+    for t in range(T):
+        if near[t]:
+            continue
+        assert sorted(ids_g[t]) == sorted(ids_o[t]), t
+        go = dict(zip(ids_o[t].tolist(), g_o[t]))
+        for j in range(FULL.top_k):
+            assert abs(g_g[t, j] - go[int(ids_g[t, j])]) <= 2e-6, (t, j)
+    assert np.all(np.abs(g_g.sum(1) - 1) < 1e-5)
+
+
+def test_router_small_shape(small):
+    x = _x(100, SMALL)
+    ids_o, g_o, gap, ids_g, g_g = _route_both(small, x)
+    ok = gap >= om.NEAR_TIE
+    assert np.array_equal(np.sort(ids_g[ok], 1), np.sort(ids_o[ok], 1))
+
+
+# --------------------------------------------------------------------------- permutation
+def _ws_int32(ws, off, n):
+    return ws[off:off + 4 * n].view(torch.int32).cpu().numpy()
+
+
+def test_permutation_exact_and_stable(full):
+    T, k, E = 333, FULL.top_k, FULL.n_experts
+    x = _x(T, FULL)
+    ids_o, g_o, _, _ = om.route(x.float().numpy(), full.w_r.numpy(), full.b.numpy(), k)
+    ids = ids_o.copy()
+    ids[5, 2] = -1      # dropped slots
+    ids[17, 0] = E + 3
+    ids_d = torch.from_numpy(ids).cuda()
+    gates = torch.from_numpy(g_o.astype(np.float32)).cuda()
+    ws = moe.workspace(_ld(FULL), "bf16", T)
+    moe.forward(x.cuda(), ids_d, gates, full.bank("bf16"), _ld(FULL), ws=ws)
+    torch.cuda.synchronize()
+    lay = moe.workspace_layout(_ld(FULL), "bf16", T)
+    flat = ids.reshape(-1)
+    valid = (flat >= 0) & (flat < E)
+    counts = _ws_int32(ws, lay["counts"], E)
+    offsets = _ws_int32(ws, lay["offsets"], E + 1)
+    assert np.array_equal(counts, np.bincount(flat[valid], minlength=E))
+    assert np.array_equal(offsets, np.concatenate([[0], np.cumsum(counts)]))
+    n = int(valid.sum())
+    src = _ws_int32(ws, lay["sorted_src"], n)
+    want = np.nonzero(valid)[0][np.argsort(flat[valid], kind="stable")]
+    assert np.array_equal(src, want)
+    inv = _ws_int32(ws, lay["inv"], T * k)
+    assert np.all(inv[~valid] == -1)
+    assert np.array_equal(inv[src], np.arange(n))
+
+
+# --------------------------------------------------------------------------- forward
+def _forward_case(L, fmt, T, outliers=False, check_act=True):
+    d = L.dims
+    x = _x(T, d, outliers)
+    xo = x.float().numpy()
+    ids_o, g_o, _, _ = om.route(xo, L.w_r.numpy(), L.b.numpy(), d.top_k)
+    g32 = g_o.astype(np.float32)
+    ws = moe.workspace(_ld(d), fmt, T)
+    y = moe.forward(x.cuda(), torch.from_numpy(ids_o).cuda(), torch.from_numpy(g32).cuda(),
+                    L.bank(fmt), _ld(d), ws=ws)
+    torch.cuda.synchronize()
+    bank_o = L.oracle_bank(fmt).preload(np.unique(ids_o), threads=16)
+    y_ref, a_ref = om.forward(xo, ids_o, g32.astype(np.float64), bank_o, return_a=True)
+    err, rms = _rel_err(y.cpu().double().numpy(), y_ref)
+    _log(f"{fmt} T={T} dims={d.hidden}x{d.ffn}: max|d|/rms = {err:.3e} (rms {rms:.3f})")
+    assert err <= TOL[fmt]
+    if check_act and fmt != "nvfp4":  # nvfp4 quantises the intermediate in place
+        lay = moe.workspace_layout(_ld(d), fmt, T)
+        R = T * d.top_k
+        src = _ws_int32(ws, lay["sorted_src"], R)
+        act = ws[lay["act"]:lay["act"] + 2 * R * d.ffn].view(torch.bfloat16).float().cpu().numpy()
+        act = act.reshape(R, d.ffn)
+        ref = a_ref[src]
+        # a = bf16(h^2): an absolute error dh of the GPU's h moves a by about
+        # 2 sqrt(a) dh on top of one bf16 ulp.  dh budget: bf16 MFMA products
+        # are exact with fp32 sums; the FP8 MFMA sums its 64 products with a
+        # shorter internal significand, so its h carries ~1e-4 relative error.
+        dh = 1e-4 if fmt == "bf16" else 3e-3
+        ulp = np.maximum(np.abs(ref), 2.0 ** -126) * 2.0 ** -7
+        bound = ulp + 2 * np.sqrt(ref) * dh + dh * dh
+        beyond_ulp = int((np.abs(act - ref) > ulp * 1.0001).sum())
+        bad = np.abs(act - ref) > bound
+        _log(f"   intermediate: {beyond_ulp} of {act.size} beyond 1 bf16 ulp, {int(bad.sum())} beyond the bound")
+        assert not bad.any()
+    return y, y_ref
+
+
+@pytest.mark.parametrize("T", [1, 4, 64, 333])
+def test_forward_bf16_full_shape(full, T):
+    _forward_case(full, "bf16", T, outliers=T > 100)
+
+
+@pytest.mark.parametrize("fmt", ["bf16", "fp8", "nvfp4"])
+@pytest.mark.parametrize("T", [3, 150, 700])
+def test_forward_small_shape(small, fmt, T):
+    _forward_case(small, fmt, T)
+
+
+@pytest.mark.parametrize("fmt", ["fp8", "nvfp4"])
+@pytest.mark.parametrize("T", [4, 64])
+def test_forward_quantised_full_shape(full, fmt, T):
+    _forward_case(full, fmt, T)
+
+
+def test_forward_bf16_output_and_determinism(full):
+    T = 64
+    x = _x(T, FULL).cuda()
+    ids, g = moe.route(x, full.w_r_d, full.b_d)
+    y1 = moe.forward(x, ids, g, full.bank("bf16"))
+    y2 = moe.forward(x, ids, g, full.bank("bf16"))
+    yb = moe.forward(x, ids, g, full.bank("bf16"), y_dtype=torch.bfloat16)
+    torch.cuda.synchronize()
+    assert torch.equal(y1, y2)  # deterministic: no atomics on the data path
+    assert torch.equal(yb, y1.to(torch.bfloat16))  # bf16 output = RNE of the fp32 result
+
+
+def test_forward_empty_and_single(full):
+    x = _x(1, FULL).cuda()
+    ids, g = moe.route(x, full.w_r_d, full.b_d)
+    y = moe.forward(x, ids, g, full.bank("bf16"))
+    y0 = moe.forward(x[:0], ids[:0], g[:0], full.bank("bf16"))
+    torch.cuda.synchronize()
+    assert y0.shape == (0, FULL.hidden)
+    assert torch.isfinite(y).all()
+
+
+# --------------------------------------------------------------------------- end to end
+def test_layer_end_to_end_decode(full):
+    T = 64
+    x = _x(T, FULL)
+    ids_o, g_o, gap, ids_g, g_g = _route_both(full, x)
+    y = moe.forward(x.cuda(), torch.from_numpy(ids_g).cuda(), torch.from_numpy(g_g).cuda(),
+                    full.bank("bf16"))
+    torch.cuda.synchronize()
+    bank_o = full.oracle_bank("bf16").preload(np.unique(ids_o), threads=16)
+    y_ref = om.forward(x.float().numpy(), ids_o, g_o, bank_o)
+    same = np.array([sorted(a) == sorted(b) for a, b in zip(ids_g, ids_o)])
+    assert np.all(same | (gap < om.NEAR_TIE))
+    err, _ = _rel_err(y.cpu().double().numpy()[same], y_ref[same])
+    assert err <= TOL["bf16"]
+
+
+def test_prefill_t4096_sampled_tokens(full):
+    # full prefill shape and launch configuration; the oracle checks a sample
+    # of tokens (each token's output depends only on its own routing)
+    T = 4096
+    x = _x(T, FULL, outliers=True)
+    xd = x.cuda()
+    ids_g, g_g = moe.route(xd, full.w_r_d, full.b_d)
+    y = moe.forward(xd, ids_g, g_g, full.bank("bf16"))
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(0)
+    out_rows = synth.outlier_rows(T)
+    sample = np.unique(np.concatenate([rng.choice(T, 40, replace=False), out_rows[:8], [0, T - 1]]))
+    xs = x[torch.from_numpy(sample)].float().numpy()
+    ids_o, g_o, gap, _ = om.route(xs, full.w_r.numpy(), full.b.numpy(), 6)
+    ig = ids_g.cpu().numpy()[sample]
+    same = np.array([sorted(a) == sorted(b) for a, b in zip(ig, ids_o)])
+    assert np.all(same | (gap < om.NEAR_TIE))
+    y_ref = om.forward(xs, ids_o, g_o, full.oracle_bank("bf16").preload(np.unique(ids_o), 16))
+    err, _ = _rel_err(y.cpu().double().numpy()[sample][same], y_ref[same])
+    _log(f"prefill sample of {len(sample)}: max|d|/rms = {err:.3e}")
+    assert err <= TOL["bf16"]
+    # every token hit exactly 6 distinct experts
+    ia = ids_g.cpu().numpy()
+    assert np.all(np.sort(ia, 1)[:, 1:] != np.sort(ia, 1)[:, :-1])
+
+
+# --------------------------------------------------------------------------- quantisers
+@pytest.mark.parametrize("fmt", ["fp8", "nvfp4"])
+def test_weight_codes_bit_exact(full, fmt):
+    bank = full.bank(fmt)
+    torch.cuda.synchronize()
+    for e in (0, 77, 127):
+        for name, w in (("up", full.up[e]), ("down", full.down[e])):
+            wf = w.float().numpy()
+            q_gpu = getattr(bank, name)[e].cpu().numpy()
+            s_gpu = getattr(bank, name + "_s")[e].item()
+            if fmt == "fp8":
+                q, s = codecs.fp8_quantize(wf)
+                assert np.array_equal(q_gpu, q), (name, e)
+            else:
+                q, sb, s = codecs.nvfp4_quantize(wf)
+                assert np.array_equal(q_gpu, codecs.nvfp4_pack(q)), (name, e)
+                assert np.array_equal(getattr(bank, name + "_bs")[e].cpu().numpy(), sb), (name, e)
+            assert np.float32(s_gpu) == np.float32(s), (name, e)
+
+
+@pytest.mark.parametrize("fmt", ["fp8", "nvfp4"])
+@pytest.mark.parametrize("T", [64, 4096])
+def test_activation_codes_bit_exact(fmt, T):
+    x = _x(T, FULL, outliers=True)
+    codes, bs, scale = moe.quantize_activation(x.cuda(), fmt)
+    torch.cuda.synchronize()
+    xf = x.float().numpy()
+    if fmt == "fp8":
+        q, s = codecs.fp8_quantize(xf)
+        assert np.array_equal(codes.cpu().numpy(), q)
+    else:
+        q, sb, s = codecs.nvfp4_quantize(xf)
+        assert np.array_equal(codes.cpu().numpy(), codecs.nvfp4_pack(q))
+        assert np.array_equal(bs.cpu().numpy(), sb)
+    assert np.float32(scale.item()) == np.float32(s)
+
+
+# --------------------------------------------------------------------------- stacked path
+def test_prenorm_and_residual(full):
+    x = _x(64, FULL, outliers=True)
+    xd = x.cuda()
+    pn = moe.prenorm(xd)
+    y = synth.make_f32((64, FULL.hidden), 6000).cuda()
+    xr = xd.clone()
+    moe.residual_add(xr, y)
+    torch.cuda.synchronize()
+    ref = om.prenorm(x.float().numpy())
+    got = pn.float().cpu().numpy()
+    ulp = np.maximum(np.abs(ref), 1e-30) * 2.0 ** -7
+    assert np.all(np.abs(got - ref) <= ulp * 1.0001)
+    ref_r = om.residual_add(x.float().numpy(), y.cpu().double().numpy())
+    assert np.array_equal(xr.float().cpu().numpy(), ref_r)
+
+
+def test_stacked_small_shape_nvfp4():
+    # a few consecutive layers with their own weights; GPU and oracle each run
+    # their own trajectory (prenorm -> route -> experts -> residual)
+    dims, T, n_layers = SMALL, 200, 3
+    x0 = _x(T, dims)
+    xg = x0.cuda().clone()
+    xo = x0.float().numpy().astype(np.float64)
+    diverged = np.zeros(T, bool)
+    for l in range(n_layers):
+        L = Layer(dims, l)
+        xin = moe.prenorm(xg)
+        ids, g = moe.route(xin, L.w_r_d, L.b_d, _ld(dims))
+        y = moe.forward(xin, ids, g, L.bank("nvfp4"), _ld(dims))
+        moe.residual_add(xg, y)
+        xin_o = om.prenorm(xo)
+        ids_o, g_o, gap, _ = om.route(xin_o, L.w_r.numpy(), L.b.numpy(), dims.top_k)
+        y_o = om.forward(xin_o, ids_o, g_o, L.oracle_bank("nvfp4"))
+        xo = om.residual_add(xo, y_o)
+        torch.cuda.synchronize()
+        same = np.array([sorted(a) == sorted(b) for a, b in zip(ids.cpu().numpy(), ids_o)])
+        assert np.all(same | (gap < om.NEAR_TIE))
+        diverged |= ~same
+    keep = ~diverged
+    err, _ = _rel_err(xg.float().cpu().numpy()[keep], xo[keep])
+    _log(f"stacked {n_layers} layers: max|d|/rms = {err:.3e}, diverged tokens {int(diverged.sum())}")
+    assert err <= TOL["nvfp4"]
