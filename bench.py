@@ -130,10 +130,11 @@ def main():
         bank = moe.quantize_experts(up_d, down_d, fmt, ld)
         if fmt != "bf16":
             del up_d, down_d
-        layers.append(dict(w_r=w_r.to(dev), b=b.to(dev), bank=bank))
+        layers.append(dict(router=moe.pack_router(w_r.to(dev), b.to(dev), ld), bank=bank))
         print(f"# layer {l} ready ({time.time() - t_setup:.1f}s)", file=sys.stderr, flush=True)
     x0 = synth.make_tokens(T, outliers=wl["outliers"]).to(dev)
     ws = moe.workspace(ld, fmt, T, dev)
+    rws = moe.route_workspace(ld, T, dev)
     y = torch.empty((T, H), dtype=torch.float32, device=dev)
     ids = torch.empty((T, k), dtype=torch.int32, device=dev)
     gates = torch.empty((T, k), dtype=torch.float32, device=dev)
@@ -147,7 +148,7 @@ def main():
         if n_layers == 1:
             if ev_route:
                 hip.record(ev_route[0], stream)
-            moe.route(x0, layers[0]["w_r"], layers[0]["b"], ld, ids=ids, gates=gates)
+            moe.route(x0, layers[0]["router"], ld, ids=ids, gates=gates, ws=rws)
             if ev_route:
                 hip.record(ev_route[1], stream)
             if ev_stages:
@@ -158,7 +159,7 @@ def main():
             xs.copy_(x0)
             for L in layers:
                 moe.prenorm(xs, xin)
-                moe.route(xin, L["w_r"], L["b"], ld, ids=ids, gates=gates)
+                moe.route(xin, L["router"], ld, ids=ids, gates=gates, ws=rws)
                 moe.forward(xin, ids, gates, L["bank"], ld, ws=ws, y=y)
                 moe.residual_add(xs, y)
 

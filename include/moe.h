@@ -70,9 +70,10 @@ typedef struct {
   int32_t hidden, ffn, n_experts, top_k;
 } moe_dims;
 
-/* [host] struct of [dev] router tensors: w fp32 [E, H]; bias fp32 [E] or NULL */
+/* [host] struct of [dev] router tensors: w_packed bf16 [3, E, H] written by
+ * moe_router_pack from the fp32 router matrix; bias fp32 [E] or NULL */
 typedef struct {
-  const float* w;
+  const void* w_packed;
   const float* bias;
 } moe_router;
 
@@ -106,16 +107,30 @@ const char* moe_status_str(int32_t status);
  * 256-byte aligned (hipMalloc and torch allocations are). */
 size_t moe_workspace_size(const moe_dims* dims, int32_t fmt, int32_t max_tokens);
 
+/* Pack the fp32 router matrix w [dev] [E, H] for moe_route: w_packed [dev]
+ * bf16 [3, E, H] = (hi, mid, lo) with w == hi + mid + lo exactly (hi and mid
+ * are truncations, lo holds the remaining <= 8 significant bits), so the
+ * router's products with bf16 tokens are exact on bf16 MFMA.  Run once per
+ * router matrix. */
+int32_t moe_router_pack(const moe_dims* dims, const float* w, void* w_packed,
+                        void* stream);
+
+/* Bytes of workspace moe_route needs for up to `max_tokens` tokens (partial
+ * logits); 0 for invalid arguments. */
+size_t moe_route_workspace_size(const moe_dims* dims, int32_t max_tokens);
+
 /* Router (bloomery issue #967, section 2: top-6 routing over 128 experts;
  * audio.cpp notes, section "CPU weight offload": routing weights are their own
  * formula).  For each token t:
  *   l_t = fp32(x_t) . W_r^T + b                (fp32 accumulation)
  *   ids[t, 0..k) = the k largest l_t,e, ordered by (logit desc, index asc)
  *   gates[t, j]  = exp(l_t,ids[j]) / sum_j' exp(l_t,ids[j'])
- * x [dev] bf16 [T, H]; ids [dev] int32 [T, k] out; gates [dev] fp32 [T, k] out. */
+ * x [dev] bf16 [T, H]; ids [dev] int32 [T, k] out; gates [dev] fp32 [T, k] out;
+ * ws [dev] workspace of ws_bytes >= moe_route_workspace_size(dims, T),
+ * 256-byte aligned. */
 int32_t moe_route(const moe_dims* dims, int32_t T, const void* x,
                   const moe_router* router, int32_t* ids, float* gates,
-                  void* stream);
+                  void* ws, size_t ws_bytes, void* stream);
 
 /* Expert part of the layer (bloomery issue #967, sections 2-3: ungated ReLU^2
  * experts 2688 -> 1856 -> 2688; audio.cpp notes, "CPU weight offload":
@@ -156,10 +171,10 @@ typedef struct {
   int64_t inv;        /* int32 [T*k]: sorted row of each flat index, -1 = dropped */
   int64_t act;        /* bf16 [T*k, F]: a = bf16(relu(h)^2), sorted row order */
   int64_t out_rows;   /* fp32 [T*k, H]: gate * W_down a~, sorted row order   */
-  int64_t x_q;        /* FP8: u8 [T, H] codes; NVFP4: bf16 [T, H] dequantised
-                         block values dec(q)*dec(sb) (tensor scale excluded) */
+  int64_t x_q;        /* bf16 [T, H] dequantised token values without the
+                         tensor scale: FP8 dec(q); NVFP4 dec(q)*dec(sb)      */
   int64_t act_q;      /* FP8: u8 [T*k, F] codes; NVFP4: in place over act    */
-  int64_t scales;     /* fp32 [4]: x scale, act scale, amax(x), amax(act)    */
+  int64_t scales;     /* fp32 [2]: x scale, act scale                        */
   int64_t total;      /* bytes                                               */
 } moe_ws_layout;
 

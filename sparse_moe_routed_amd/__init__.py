@@ -6,7 +6,8 @@ HIP stream.  There is no fallback: if the library is missing or no GPU is
 visible, the compute calls raise.
 
     import sparse_moe_routed_amd as moe
-    ids, gates = moe.route(x, w_r, b)                 # top-6 routing
+    router = moe.pack_router(w_r, b)                  # once per router matrix
+    ids, gates = moe.route(x, router)                 # top-6 routing
     y = moe.forward(x, ids, gates, experts)           # routed experts
 """
 from __future__ import annotations
@@ -19,7 +20,7 @@ from typing import Optional
 import torch
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_PKG, "libmoe.so")
+LIB_PATH = os.environ.get("MOE_LIB") or os.path.join(_PKG, "libmoe.so")
 
 OK, EINVAL, EUNSUPPORTED, EWORKSPACE, EHIP = 0, 1, 2, 3, 4
 WFMT = {"bf16": 0, "fp8": 1, "nvfp4": 2}
@@ -38,7 +39,7 @@ class Dims(ctypes.Structure):
 
 
 class Router(ctypes.Structure):
-    _fields_ = [("w", ctypes.c_void_p), ("bias", ctypes.c_void_p)]
+    _fields_ = [("w_packed", ctypes.c_void_p), ("bias", ctypes.c_void_p)]
 
 
 class Experts(ctypes.Structure):
@@ -60,9 +61,12 @@ _SIGS = {
     "moe_workspace_size": (ctypes.c_size_t, [ctypes.POINTER(Dims), ctypes.c_int32, ctypes.c_int32]),
     "moe_workspace_layout": (ctypes.c_int32, [ctypes.POINTER(Dims), ctypes.c_int32, ctypes.c_int32,
                                               ctypes.POINTER(WsLayout)]),
+    "moe_router_pack": (ctypes.c_int32, [ctypes.POINTER(Dims), ctypes.c_void_p, ctypes.c_void_p,
+                                         ctypes.c_void_p]),
+    "moe_route_workspace_size": (ctypes.c_size_t, [ctypes.POINTER(Dims), ctypes.c_int32]),
     "moe_route": (ctypes.c_int32, [ctypes.POINTER(Dims), ctypes.c_int32, ctypes.c_void_p,
                                    ctypes.POINTER(Router), ctypes.c_void_p, ctypes.c_void_p,
-                                   ctypes.c_void_p]),
+                                   ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]),
     "moe_forward": (ctypes.c_int32, [ctypes.POINTER(Dims), ctypes.c_int32, ctypes.c_void_p,
                                      ctypes.c_void_p, ctypes.c_void_p, ctypes.POINTER(Experts),
                                      ctypes.c_void_p, ctypes.c_int32, ctypes.c_void_p,
@@ -184,25 +188,52 @@ def workspace(dims: LayerDims, fmt: str, max_tokens: int, device="cuda") -> torc
     return torch.empty(max(256, workspace_size(dims, fmt, max_tokens)), dtype=torch.uint8, device=device)
 
 
-def route(x: torch.Tensor, w_r: torch.Tensor, bias: Optional[torch.Tensor] = None,
-          dims: LayerDims = LayerDims(), ids: Optional[torch.Tensor] = None,
-          gates: Optional[torch.Tensor] = None):
-    """moe_route: ids int32 [T, k], gates fp32 [T, k]."""
-    T = x.shape[0]
-    _dev(x, torch.bfloat16, "x", (T, dims.hidden))
+@dataclass
+class PackedRouter:
+    """Router matrix packed by moe_router_pack (bf16 [3, E, H]) and its bias."""
+    w_packed: torch.Tensor
+    bias: Optional[torch.Tensor] = None
+
+
+def pack_router(w_r: torch.Tensor, bias: Optional[torch.Tensor] = None,
+                dims: LayerDims = LayerDims()) -> PackedRouter:
+    """moe_router_pack: fp32 [E, H] -> exact bf16 (hi, mid, lo) split."""
     _dev(w_r, torch.float32, "w_r", (dims.n_experts, dims.hidden))
     if bias is not None:
         _dev(bias, torch.float32, "bias", (dims.n_experts,))
+    packed = torch.empty((3, dims.n_experts, dims.hidden), dtype=torch.bfloat16, device=w_r.device)
+    d = dims.c()
+    _check("moe_router_pack", lib().moe_router_pack(ctypes.byref(d), _ptr(w_r), _ptr(packed), _stream()))
+    return PackedRouter(packed, bias)
+
+
+def route_workspace(dims: LayerDims, max_tokens: int, device="cuda") -> torch.Tensor:
+    d = dims.c()
+    n = int(lib().moe_route_workspace_size(ctypes.byref(d), int(max_tokens)))
+    return torch.empty(max(256, n), dtype=torch.uint8, device=device)
+
+
+def route(x: torch.Tensor, router: PackedRouter, dims: LayerDims = LayerDims(),
+          ids: Optional[torch.Tensor] = None, gates: Optional[torch.Tensor] = None,
+          ws: Optional[torch.Tensor] = None):
+    """moe_route: ids int32 [T, k], gates fp32 [T, k]."""
+    T = x.shape[0]
+    _dev(x, torch.bfloat16, "x", (T, dims.hidden))
+    _dev(router.w_packed, torch.bfloat16, "w_packed", (3, dims.n_experts, dims.hidden))
     if ids is None:
         ids = torch.empty((T, dims.top_k), dtype=torch.int32, device=x.device)
     if gates is None:
         gates = torch.empty((T, dims.top_k), dtype=torch.float32, device=x.device)
+    if ws is None:
+        ws = route_workspace(dims, T, x.device)
     _dev(ids, torch.int32, "ids", (T, dims.top_k))
     _dev(gates, torch.float32, "gates", (T, dims.top_k))
+    _dev(ws, torch.uint8, "ws")
     d = dims.c()
-    r = Router(w_r.data_ptr(), bias.data_ptr() if bias is not None else None)
+    r = Router(router.w_packed.data_ptr(),
+               router.bias.data_ptr() if router.bias is not None else None)
     _check("moe_route", lib().moe_route(ctypes.byref(d), T, _ptr(x), ctypes.byref(r), _ptr(ids),
-                                        _ptr(gates), _stream()))
+                                        _ptr(gates), _ptr(ws), ws.numel(), _stream()))
     return ids, gates
 
 

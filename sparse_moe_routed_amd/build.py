@@ -46,9 +46,9 @@ def sources():
     return sorted(os.path.join(CSRC, f) for f in os.listdir(CSRC) if f.endswith(".hip"))
 
 
-def _compile(src: str) -> str:
-    obj = os.path.join(OBJDIR, os.path.basename(src) + ".o")
-    cmd = [hipcc(), *HIPCC_FLAGS, "-c", src, "-o", obj]
+def _compile(src: str, objdir: str = OBJDIR, extra=()) -> str:
+    obj = os.path.join(objdir, os.path.basename(src) + ".o")
+    cmd = [hipcc(), *HIPCC_FLAGS, *extra, "-c", src, "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     noise = "is not a recognized feature for this target"
     err = "\n".join(l for l in (r.stderr or "").splitlines() if noise not in l)
@@ -59,20 +59,22 @@ def _compile(src: str) -> str:
     return obj
 
 
-def build(verbose: bool = True) -> str:
-    os.makedirs(OBJDIR, exist_ok=True)
+def build(verbose: bool = True, out: str = OUT, defines=()) -> str:
+    objdir = OBJDIR if out == OUT else os.path.join(ROOT, "_build", "obj_" + os.path.basename(out))
+    os.makedirs(objdir, exist_ok=True)
     srcs = sources()
+    extra = [f"-D{d}" for d in defines]
     with ThreadPoolExecutor(max(1, min(8, len(srcs)))) as ex:
-        objs = list(ex.map(_compile, srcs))
-    tmp = OUT + ".tmp"
+        objs = list(ex.map(lambda s_: _compile(s_, objdir, extra), srcs))
+    tmp = out + ".tmp"
     cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError("link failed:\n" + r.stderr)
-    os.replace(tmp, OUT)
+    os.replace(tmp, out)
     if verbose:
-        print(f"built {OUT} from {len(srcs)} sources")
-    return OUT
+        print(f"built {out} from {len(srcs)} sources")
+    return out
 
 
 if __name__ == "__main__":

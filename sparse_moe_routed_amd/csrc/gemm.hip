@@ -8,7 +8,8 @@
 //
 // One kernel template serves both projections and all three weight formats.
 // A workgroup computes a BM x BN tile of one expert: BM sorted rows of that
-// expert (from the permutation's device tile list) times BN output columns.
+// expert (row tiles counted by the permutation on the device) times BN output
+// columns.
 // Both operands are K-contiguous; each K step moves 128 bytes of every A and
 // B row through double-buffered LDS (rows padded to 144 bytes, which keeps
 // the 16-byte MFMA operand reads of 16 consecutive rows on distinct banks).
@@ -18,12 +19,22 @@
 //          is zero-filled in LDS rather than padded in HBM (zero padding of K
 //          with matching zero activations leaves results unchanged: audio.cpp
 //          notes, section "Q4_K, Q3_K and Q2_K expert profiles").
-//   NVFP4: E2M1 codes and E4M3 block scales are expanded to bf16 while being
-//          staged into LDS (code * block scale has at most 6 significant bits,
-//          so the bf16 value is exact), then the BF16 MFMA; the two fp32 tensor
-//          scales are applied in the epilogue.
+//   FP8X : E4M3 weight codes expanded to bf16 while staged into LDS
+//          (v_cvt_scalef32_pk_bf16_fp8 with unit scale, exact), then the BF16
+//          MFMA on bf16 activations holding dec(code).  Used for the FP8 up
+//          projection: the FP8 MFMA sums its 64 products with a short internal
+//          significand (about 13 bits below the largest product), and the up
+//          projection's output is re-quantised, so that error would move
+//          intermediate E4M3 codes; exact products with fp32 sums do not.
+//   NVFP4: E2M1 codes expanded with v_cvt_scalef32_pk_bf16_fp4 (unit scale)
+//          and multiplied by the E4M3 block scale in fp32 (code * block scale
+//          has at most 6 significant bits, so the bf16 value is exact), then
+//          the BF16 MFMA; the two fp32 tensor scales are applied in the
+//          epilogue.
 // Epilogues: up writes bf16(relu(h)^2) (and the tensor amax for quantised
 // formats); down writes fp32 gate * h per sorted row.
+#include <type_traits>
+
 #include "moe_common.h"
 #include "moe_internal.h"
 
@@ -39,27 +50,44 @@ __global__ __launch_bounds__(WM* WN * 64) void grouped_gemm_kernel(GemmArgs g) {
   constexpr int NT = WM * WN * 64;
   constexpr int WTM = BM / WM, WTN = BN / WN;  // wave tile
   constexpr int MB = WTM / 32, NB = WTN / 32;  // 32x32 MFMA blocks per wave
-  constexpr int A_CH = BM * 8 / NT;            // 16-byte A chunks per thread per step
-  constexpr int B_CH = (FMT == kNVFP4) ? (BN * 2 / NT) : (BN * 8 / NT);
+  // 16-byte source chunks per step: A rows 8 each; B rows 8 (bf16 / fp8),
+  // 4 (fp8 expanded: 64 codes) or 2 (nvfp4: 64 codes packed).  When a tile has
+  // fewer chunks than threads, the extra threads repeat a chunk (same data to
+  // the same LDS bytes), which keeps the loads branch-free.
+  constexpr int A_TOT = BM * 8;
+  constexpr int B_TOT = (FMT == kNVFP4) ? BN * 2 : (FMT == kFP8X ? BN * 4 : BN * 8);
+  constexpr int A_CH = (A_TOT + NT - 1) / NT;
+  constexpr int B_CH = (B_TOT + NT - 1) / NT;
   constexpr int ESZ = (FMT == kFP8) ? 1 : 2;   // bytes per staged element
   static_assert(MB >= 1 && NB >= 1 && A_CH >= 1 && B_CH >= 1, "tile shape");
-  static_assert((BM * 8) % NT == 0, "A chunks");
 
   __shared__ __attribute__((aligned(16))) uint8_t lds[2 * (BM + BN) * kLds];
   uint8_t* const As = lds;
   uint8_t* const Bs = lds + 2 * BM * kLds;
 
-  // ---- which tile: blocks are dealt round-robin to the 8 XCDs; give each
-  // XCD a contiguous run of logical tiles so the row tiles of one expert and
-  // column tile (same weight panel) share that XCD's L2.
-  const int nblk = gridDim.x;  // a multiple of 8
-  const int logical = (blockIdx.x & 7) * (nblk >> 3) + (blockIdx.x >> 3);
+  // ---- which tile.  Logical tiles run expert-major, then column tile, then
+  // row tile, so one expert's activation rows and each weight panel are used
+  // by tiles that run at the same time.  Blocks are dealt round-robin to the
+  // 8 XCDs; each XCD takes a contiguous 1/8 of the logical tiles, so an
+  // expert's rows and weights stay in one XCD's L2.
   const int n_ntiles = (g.N + BN - 1) / BN;
-  const int ntile = logical / g.max_tiles;
-  const int mt = logical - ntile * g.max_tiles;
-  if (ntile >= n_ntiles || mt >= *g.n_tiles) return;
-  const int2 tile = g.tiles[mt];
-  const int e = tile.x, row0 = tile.y;
+  const int total = g.tile_off[g.E] * n_ntiles;
+  const int per_xcd = (total + 7) >> 3;
+  const int local = blockIdx.x >> 3;
+  if (local >= per_xcd) return;
+  const int logical = (blockIdx.x & 7) * per_xcd + local;
+  if (logical >= total) return;
+  int lo = 0, hi = g.E;  // largest e with tile_off[e] * n_ntiles <= logical
+  while (hi - lo > 1) {
+    const int mid = (lo + hi) >> 1;
+    if (g.tile_off[mid] * n_ntiles <= logical) lo = mid; else hi = mid;
+  }
+  const int e = lo;
+  const int te = g.tile_off[e + 1] - g.tile_off[e];
+  const int loc = logical - g.tile_off[e] * n_ntiles;
+  const int ntile = loc / te;
+  const int mt = loc - ntile * te;
+  const int row0 = g.offsets[e] + mt * BM;
   const int rows_valid = min(BM, g.offsets[e + 1] - row0);
   const int n0 = ntile * BN;
 
@@ -74,7 +102,7 @@ __global__ __launch_bounds__(WM* WN * 64) void grouped_gemm_kernel(GemmArgs g) {
   int a_dst[A_CH], a_col[A_CH];
 #pragma unroll
   for (int i = 0; i < A_CH; ++i) {
-    const int c = tid + i * NT;
+    const int c = (tid + i * NT) % A_TOT;
     const int r = c >> 3, cc = c & 7;
     const int rr = min(r, rows_valid - 1);
     size_t src;
@@ -92,7 +120,7 @@ __global__ __launch_bounds__(WM* WN * 64) void grouped_gemm_kernel(GemmArgs g) {
   int b_dst[B_CH], b_col[B_CH];
 #pragma unroll
   for (int i = 0; i < B_CH; ++i) {
-    const int c = tid + i * NT;
+    const int c = (tid + i * NT) % B_TOT;
     if constexpr (FMT == kNVFP4) {
       const int r = c >> 1, half = c & 1;
       const int n = min(n0 + r, N - 1);
@@ -100,6 +128,14 @@ __global__ __launch_bounds__(WM* WN * 64) void grouped_gemm_kernel(GemmArgs g) {
       b_src[i] = static_cast<const uint8_t*>(g.b) + row * (K / 2) + half * 16;
       s_src[i] = g.b_bs + row * (K / 16) + half * 2;
       b_dst[i] = r * kLds + half * 64;
+      b_col[i] = 0;
+    } else if constexpr (FMT == kFP8X) {
+      const int r = c >> 2, q = c & 3;  // 16 codes of the row's 64 per step
+      const int n = min(n0 + r, N - 1);
+      const size_t row = static_cast<size_t>(e) * N + n;
+      b_src[i] = static_cast<const uint8_t*>(g.b) + row * K + q * 16;
+      s_src[i] = nullptr;
+      b_dst[i] = r * kLds + q * 32;
       b_col[i] = 0;
     } else {
       const int r = c >> 3, cc = c & 7;
@@ -112,56 +148,75 @@ __global__ __launch_bounds__(WM* WN * 64) void grouped_gemm_kernel(GemmArgs g) {
     }
   }
 
-  u32x4 a_reg[A_CH];
-  u32x4 b_reg[B_CH];
-  uint32_t s_reg[B_CH];
+  // two register sets: the loads of steps s+1 and s+2 are in flight while
+  // step s is multiplied out of LDS
+  u32x4 a_reg[2][A_CH];
+  u32x4 b_reg[2][B_CH];
+  uint32_t s_reg[2][B_CH];
 
-  auto load = [&](int step) {
+  // Loads are issued unconditionally (no branches around vector memory ops,
+  // so the compiler can wait for exactly the set it needs): steps past the end
+  // re-read the last step, and the FP8 K tail reads an in-range chunk and
+  // replaces it by zeros.
+  auto load = [&](int step_in, auto set_c) {
+    constexpr int SET = decltype(set_c)::value;
+    const int step = min(step_in, n_steps - 1);
     const int kb = step * kStepBytes;
 #pragma unroll
     for (int i = 0; i < A_CH; ++i) {
-      if (FMT == kFP8 && kb + a_col[i] >= k_bytes) {
-        a_reg[i] = u32x4{0u, 0u, 0u, 0u};
+      if constexpr (FMT == kFP8) {
+        const bool tail = kb + a_col[i] >= k_bytes;
+        const u32x4 v = *reinterpret_cast<const u32x4*>(a_src[i] + (tail ? kb - 64 : kb));
+        a_reg[SET][i] = tail ? u32x4{0u, 0u, 0u, 0u} : v;
       } else {
-        a_reg[i] = *reinterpret_cast<const u32x4*>(a_src[i] + kb);
+        a_reg[SET][i] = *reinterpret_cast<const u32x4*>(a_src[i] + kb);
       }
     }
 #pragma unroll
     for (int i = 0; i < B_CH; ++i) {
       if constexpr (FMT == kNVFP4) {
-        b_reg[i] = *reinterpret_cast<const u32x4*>(b_src[i] + step * 32);
-        s_reg[i] = *reinterpret_cast<const uint16_t*>(s_src[i] + step * 4);
+        b_reg[SET][i] = *reinterpret_cast<const u32x4*>(b_src[i] + step * 32);
+        s_reg[SET][i] = *reinterpret_cast<const uint16_t*>(s_src[i] + step * 4);
+      } else if constexpr (FMT == kFP8X) {
+        b_reg[SET][i] = *reinterpret_cast<const u32x4*>(b_src[i] + step * 64);
+      } else if constexpr (FMT == kFP8) {
+        const bool tail = kb + b_col[i] >= k_bytes;
+        const u32x4 v = *reinterpret_cast<const u32x4*>(b_src[i] + (tail ? kb - 64 : kb));
+        b_reg[SET][i] = tail ? u32x4{0u, 0u, 0u, 0u} : v;
       } else {
-        if (FMT == kFP8 && kb + b_col[i] >= k_bytes) {
-          b_reg[i] = u32x4{0u, 0u, 0u, 0u};
-        } else {
-          b_reg[i] = *reinterpret_cast<const u32x4*>(b_src[i] + kb);
-        }
+        b_reg[SET][i] = *reinterpret_cast<const u32x4*>(b_src[i] + kb);
       }
     }
   };
 
-  auto store = [&](int buf) {
+  auto store = [&](int buf, auto set_c) {
+    constexpr int SET = decltype(set_c)::value;
     uint8_t* A = As + buf * BM * kLds;
     uint8_t* B = Bs + buf * BN * kLds;
 #pragma unroll
-    for (int i = 0; i < A_CH; ++i) *reinterpret_cast<u32x4*>(A + a_dst[i]) = a_reg[i];
+    for (int i = 0; i < A_CH; ++i) *reinterpret_cast<u32x4*>(A + a_dst[i]) = a_reg[SET][i];
 #pragma unroll
     for (int i = 0; i < B_CH; ++i) {
       if constexpr (FMT == kNVFP4) {
         // 32 E2M1 codes (element 2j in the low nibble of byte j), two block scales
-        const float sc0 = e4m3_decode(s_reg[i] & 0xffu);
-        const float sc1 = e4m3_decode((s_reg[i] >> 8) & 0xffu);
+        const float sc0 = e4m3_decode(s_reg[SET][i] & 0xffu);
+        const float sc1 = e4m3_decode((s_reg[SET][i] >> 8) & 0xffu);
         uint32_t outw[16];
 #pragma unroll
         for (int w = 0; w < 4; ++w) {
-          const uint32_t word = b_reg[i][w];
+          const uint32_t word = b_reg[SET][i][w];
           const float sc = w < 2 ? sc0 : sc1;
+          // two E2M1 values per byte as bf16 (unit scale: exact), times the block scale
+          bf16x2 p[4];
+          p[0] = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(word, 1.0f, 0);
+          p[1] = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(word, 1.0f, 1);
+          p[2] = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(word, 1.0f, 2);
+          p[3] = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(word, 1.0f, 3);
 #pragma unroll
           for (int bb = 0; bb < 4; ++bb) {
-            const uint32_t byte = (word >> (8 * bb)) & 0xffu;
-            const float v0 = e2m1_decode(byte & 15u) * sc;  // exact
-            const float v1 = e2m1_decode(byte >> 4) * sc;
+            const uint32_t pw = __builtin_bit_cast(uint32_t, p[bb]);
+            const float v0 = __uint_as_float(pw << 16) * sc;
+            const float v1 = __uint_as_float(pw & 0xffff0000u) * sc;
             outw[w * 4 + bb] = (__float_as_uint(v0) >> 16) | (__float_as_uint(v1) & 0xffff0000u);
           }
         }
@@ -169,13 +224,28 @@ __global__ __launch_bounds__(WM* WN * 64) void grouped_gemm_kernel(GemmArgs g) {
 #pragma unroll
         for (int q = 0; q < 4; ++q)
           dst[q] = u32x4{outw[4 * q], outw[4 * q + 1], outw[4 * q + 2], outw[4 * q + 3]};
+      } else if constexpr (FMT == kFP8X) {
+        // 16 E4M3 codes -> 16 bf16 (unit scale: exact)
+        uint32_t outw[8];
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+          const bf16x2 lo = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(b_reg[SET][i][w], 1.0f, false);
+          const bf16x2 hi = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(b_reg[SET][i][w], 1.0f, true);
+          outw[2 * w] = __builtin_bit_cast(uint32_t, lo);
+          outw[2 * w + 1] = __builtin_bit_cast(uint32_t, hi);
+        }
+        u32x4* dst = reinterpret_cast<u32x4*>(B + b_dst[i]);
+        dst[0] = u32x4{outw[0], outw[1], outw[2], outw[3]};
+        dst[1] = u32x4{outw[4], outw[5], outw[6], outw[7]};
       } else {
-        *reinterpret_cast<u32x4*>(B + b_dst[i]) = b_reg[i];
+        *reinterpret_cast<u32x4*>(B + b_dst[i]) = b_reg[SET][i];
       }
     }
   };
 
-  // ---- which MFMA blocks of this wave hold live rows / columns
+  // ---- which MFMA blocks of this wave hold live rows / columns (the epilogue
+  // stores only those; the main loop multiplies every block without branches,
+  // dead rows and columns hold clamped copies of live ones)
   bool m_live[MB], n_live[NB];
 #pragma unroll
   for (int i = 0; i < MB; ++i) m_live[i] = wm * WTM + i * 32 < rows_valid;
@@ -193,7 +263,12 @@ __global__ __launch_bounds__(WM* WN * 64) void grouped_gemm_kernel(GemmArgs g) {
   const int lrow = lane & 31;
   const int lk = lane >> 5;  // which K half of a sub-step this lane supplies
 
+  // a wave whose 64-row band holds no live row skips its MFMAs (the branch
+  // is wave-uniform; its LDS reads stay inside it)
+  const bool wave_live = __builtin_amdgcn_readfirstlane(wm * WTM < rows_valid ? 1 : 0) != 0;
+
   auto compute = [&](int buf) {
+    if (!wave_live) return;
     const uint8_t* A = As + buf * BM * kLds;
     const uint8_t* B = Bs + buf * BN * kLds;
     if constexpr (FMT == kFP8) {
@@ -220,8 +295,7 @@ __global__ __launch_bounds__(WM* WN * 64) void grouped_gemm_kernel(GemmArgs g) {
         for (int i = 0; i < MB; ++i)
 #pragma unroll
           for (int j = 0; j < NB; ++j)
-            if (m_live[i] && n_live[j])
-              acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+            acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
                   af[i], bfr[j], acc[i][j], 0, 0, 0, 127, 0, 127);
       }
     } else {
@@ -240,23 +314,31 @@ __global__ __launch_bounds__(WM* WN * 64) void grouped_gemm_kernel(GemmArgs g) {
         for (int i = 0; i < MB; ++i)
 #pragma unroll
           for (int j = 0; j < NB; ++j)
-            if (m_live[i] && n_live[j])
-              acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
+            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
       }
     }
   };
 
-  // ---- main loop: one barrier per K step (double-buffered LDS)
-  load(0);
-  store(0);
+  // ---- main loop: one barrier per K step (double-buffered LDS, loads two
+  // steps ahead).  Unrolled by two so register sets are compile-time indices;
+  // an odd step count runs one extra iteration that stores but does not compute.
+  using S0 = std::integral_constant<int, 0>;
+  using S1 = std::integral_constant<int, 1>;
+  load(0, S0{});
+  load(1, S1{});
+  store(0, S0{});
+  load(2, S0{});
   __syncthreads();
-  for (int step = 0; step < n_steps; ++step) {
-    const int buf = step & 1;
-    const bool more = step + 1 < n_steps;
-    if (more) load(step + 1);
-    compute(buf);
-    if (more) store(buf ^ 1);
+  auto iter = [&](int step, auto set_next) {
+    // data of step+1 sits in register set (step+1)&1 == set_next
+    if (step < n_steps) compute(step & 1);
+    store((step + 1) & 1, set_next);
+    load(step + 3, set_next);
     __syncthreads();
+  };
+  for (int step = 0; step < n_steps; step += 2) {
+    iter(step, S1{});
+    iter(step + 1, S0{});
   }
 
   // ---- epilogue.  32x32 f32 result: lane holds column lane%32 and rows
@@ -298,10 +380,7 @@ __global__ __launch_bounds__(WM* WN * 64) void grouped_gemm_kernel(GemmArgs g) {
       }
     }
   }
-  if constexpr (STAGE == 0 && FMT != kBF16) {
-    local_max = wave_max(local_max);
-    if (lane == 0) atomic_max_nonneg(g.amax, local_max);
-  }
+  if constexpr (STAGE == 0 && FMT != kBF16) block_amax_to_slots(local_max, g.amax);
 }
 
 template <int FMT, int STAGE, int BM, int BN, int WM, int WN>
@@ -315,25 +394,60 @@ hipError_t launch_one(const GemmArgs& g, hipStream_t stream) {
   return hipGetLastError();
 }
 
+// Prefill tile shape (rows x columns, waves in M x N); kept as one switch so
+// alternative shapes can be compared by rebuilding with MOE_PREFILL_CFG.
+#ifndef MOE_PREFILL_CFG
+#define MOE_PREFILL_CFG 2
+#endif
+#if MOE_PREFILL_CFG == 0
+constexpr int kPBM = 128, kPBN = 128, kPWM = 2, kPWN = 2;
+#elif MOE_PREFILL_CFG == 1
+constexpr int kPBM = 128, kPBN = 256, kPWM = 2, kPWN = 2;
+#elif MOE_PREFILL_CFG == 2
+constexpr int kPBM = 128, kPBN = 128, kPWM = 2, kPWN = 4;
+#elif MOE_PREFILL_CFG == 3
+constexpr int kPBM = 256, kPBN = 128, kPWM = 4, kPWN = 2;
+#elif MOE_PREFILL_CFG == 4
+constexpr int kPBM = 64, kPBN = 256, kPWM = 1, kPWN = 4;
+#elif MOE_PREFILL_CFG == 5
+constexpr int kPBM = 128, kPBN = 256, kPWM = 2, kPWN = 4;
+#elif MOE_PREFILL_CFG == 6
+constexpr int kPBM = 128, kPBN = 384, kPWM = 2, kPWN = 6;
+#elif MOE_PREFILL_CFG == 7
+constexpr int kPBM = 64, kPBN = 384, kPWM = 1, kPWN = 6;
+#elif MOE_PREFILL_CFG == 8
+constexpr int kPBM = 128, kPBN = 192, kPWM = 2, kPWN = 3;
+#elif MOE_PREFILL_CFG == 9
+constexpr int kPBM = 64, kPBN = 256, kPWM = 2, kPWN = 4;
+#elif MOE_PREFILL_CFG == 10
+constexpr int kPBM = 256, kPBN = 256, kPWM = 4, kPWN = 2;
+#elif MOE_PREFILL_CFG == 11
+constexpr int kPBM = 256, kPBN = 128, kPWM = 4, kPWN = 2;
+#elif MOE_PREFILL_CFG == 12
+constexpr int kPBM = 128, kPBN = 256, kPWM = 2, kPWN = 2;
+#else
+#error "unknown MOE_PREFILL_CFG"
+#endif
+
 template <int FMT, int STAGE>
 hipError_t launch_fmt_stage(int T, const GemmArgs& g, hipStream_t stream) {
   const GemmShape s = gemm_shape(FMT, STAGE, T);
   if (s.bm == 32) return launch_one<FMT, STAGE, 32, 128, 1, 4>(g, stream);
-  return launch_one<FMT, STAGE, 128, 128, 2, 2>(g, stream);
+  return launch_one<FMT, STAGE, kPBM, kPBN, kPWM, kPWN>(g, stream);
 }
 
 }  // namespace
 
 GemmShape gemm_shape(int /*fmt*/, int /*stage*/, int T) {
   if (T < 512) return GemmShape{32, 128};
-  return GemmShape{128, 128};
+  return GemmShape{kPBM, kPBN};
 }
 
 hipError_t launch_gemm(int fmt, int stage, int T, const GemmArgs& g, hipStream_t stream) {
   switch (fmt * 2 + stage) {
     case kBF16 * 2 + 0: return launch_fmt_stage<kBF16, 0>(T, g, stream);
     case kBF16 * 2 + 1: return launch_fmt_stage<kBF16, 1>(T, g, stream);
-    case kFP8 * 2 + 0: return launch_fmt_stage<kFP8, 0>(T, g, stream);
+    case kFP8 * 2 + 0: return launch_fmt_stage<kFP8X, 0>(T, g, stream);
     case kFP8 * 2 + 1: return launch_fmt_stage<kFP8, 1>(T, g, stream);
     case kNVFP4 * 2 + 0: return launch_fmt_stage<kNVFP4, 0>(T, g, stream);
     case kNVFP4 * 2 + 1: return launch_fmt_stage<kNVFP4, 1>(T, g, stream);

@@ -7,6 +7,7 @@
 #include <limits>
 
 #include "../../include/moe.h"
+#include "moe_common.h"
 #include "moe_internal.h"
 
 namespace {
@@ -36,14 +37,14 @@ bool dims_ok(const moe_dims* d) { return dims_check(d) == MOE_OK; }
 bool fmt_ok(int32_t fmt) { return fmt == kBF16 || fmt == kFP8 || fmt == kNVFP4; }
 
 struct Layout {
-  size_t counts, offsets, ctrl, scales, chunk_counts, chunk_base, tiles0, tiles1, sorted_src,
+  size_t counts, offsets, scales, chunk_counts, chunk_base, tile_off0, tile_off1, sorted_src,
       inv, row_gate, act, out_rows, x_q, act_q, total;
   bool has_xq, has_actq, actq_inplace;
   int max_tiles;
 };
 
-// ctrl words: [0] n_tiles0, [1] n_tiles1; scales floats: [0] x scale, [1] act scale,
-// [2] amax(x) bits, [3] amax(act) bits
+// scales floats: [0] x scale, [1] act scale; then the amax slots of x and of
+// the intermediate (kAmaxSlots words each, fp32 bits)
 Layout make_layout(const moe_dims* d, int32_t fmt, int32_t T) {
   Layout L{};
   const size_t E = static_cast<size_t>(d->n_experts);
@@ -60,12 +61,11 @@ Layout make_layout(const moe_dims* d, int32_t fmt, int32_t T) {
   };
   L.counts = alloc(E * 4);
   L.offsets = alloc((E + 1) * 4);
-  L.ctrl = alloc(16 * 4);
-  L.scales = alloc(16 * 4);
+  L.scales = alloc((16 + 2 * moe::kAmaxSlots) * 4);
   L.chunk_counts = alloc(n_chunks * E * 4);
   L.chunk_base = alloc(n_chunks * E * 4);
-  L.tiles0 = alloc(max_tiles * 8);
-  L.tiles1 = alloc(max_tiles * 8);
+  L.tile_off0 = alloc((E + 1) * 4);
+  L.tile_off1 = alloc((E + 1) * 4);
   L.sorted_src = alloc(R * 4);
   L.inv = alloc(R * 4);
   L.row_gate = alloc(R * 4);
@@ -74,7 +74,7 @@ Layout make_layout(const moe_dims* d, int32_t fmt, int32_t T) {
   L.has_xq = fmt != kBF16;
   L.has_actq = fmt != kBF16;
   L.actq_inplace = fmt == kNVFP4;
-  L.x_q = L.has_xq ? alloc(static_cast<size_t>(T) * H * (fmt == kFP8 ? 1 : 2)) : 0;
+  L.x_q = L.has_xq ? alloc(static_cast<size_t>(T) * H * 2) : 0;
   L.act_q = fmt == kFP8 ? alloc(R * F) : L.act;
   L.total = (off + kAlign - 1) / kAlign * kAlign;
   L.max_tiles = static_cast<int>(max_tiles);
@@ -126,15 +126,35 @@ int32_t moe_workspace_layout(const moe_dims* dims, int32_t fmt, int32_t T, moe_w
   return MOE_OK;
 }
 
+size_t moe_route_workspace_size(const moe_dims* dims, int32_t max_tokens) {
+  if (!dims_ok(dims) || max_tokens < 0 || max_tokens > kMaxTokens) return 0;
+  const size_t bytes = static_cast<size_t>(moe::router_k_slices(1, dims->hidden)) *
+                       static_cast<size_t>(max_tokens) * dims->n_experts * 4;
+  return bytes < kAlign ? kAlign : (bytes + kAlign - 1) / kAlign * kAlign;
+}
+
+int32_t moe_router_pack(const moe_dims* dims, const float* w, void* w_packed, void* stream) {
+  if (const moe_status ds = dims_check(dims)) return ds;
+  if (!w || !w_packed) return MOE_EINVAL;
+  return hip_status(moe::launch_router_pack(w, dims->n_experts, dims->hidden,
+                                            static_cast<uint16_t*>(w_packed),
+                                            static_cast<hipStream_t>(stream)));
+}
+
 int32_t moe_route(const moe_dims* dims, int32_t T, const void* x, const moe_router* router,
-                  int32_t* ids, float* gates, void* stream) {
+                  int32_t* ids, float* gates, void* ws, size_t ws_bytes, void* stream) {
   if (const moe_status ds = dims_check(dims)) return ds;
   if (T < 0 || T > kMaxTokens) return MOE_EINVAL;
   if (T == 0) return MOE_OK;  // nothing is read or written; pointers may be null
-  if (!router || !router->w || !x || !ids || !gates) return MOE_EINVAL;
-  return hip_status(moe::launch_router(static_cast<const uint16_t*>(x), router->w, router->bias,
-                                       T, dims->hidden, dims->n_experts, dims->top_k, ids,
-                                       gates, static_cast<hipStream_t>(stream)));
+  if (!router || !router->w_packed || !x || !ids || !gates) return MOE_EINVAL;
+  const size_t need = static_cast<size_t>(moe::router_k_slices(T, dims->hidden)) * T *
+                      dims->n_experts * 4;
+  if (!ws || ws_bytes < need || reinterpret_cast<uintptr_t>(ws) % kAlign) return MOE_EWORKSPACE;
+  return hip_status(moe::launch_router(static_cast<const uint16_t*>(x),
+                                       static_cast<const uint16_t*>(router->w_packed),
+                                       router->bias, T, dims->hidden, dims->n_experts,
+                                       dims->top_k, static_cast<float*>(ws), ids, gates,
+                                       static_cast<hipStream_t>(stream)));
 }
 
 }  // extern "C"
@@ -173,10 +193,9 @@ int32_t forward_impl(const moe_dims* dims, int32_t T, const void* x, const int32
   const int fmt = ex->fmt;
   const int H = dims->hidden, F = dims->ffn, E = dims->n_experts, k = dims->top_k;
   const int R = T * k;
-  int32_t* ctrl = at<int32_t>(ws, L.ctrl);
   float* scales = at<float>(ws, L.scales);
-  uint32_t* amax_x = reinterpret_cast<uint32_t*>(scales + 2);
-  uint32_t* amax_a = reinterpret_cast<uint32_t*>(scales + 3);
+  uint32_t* amax_x = reinterpret_cast<uint32_t*>(scales + 16);
+  uint32_t* amax_a = amax_x + moe::kAmaxSlots;
   int32_t* offsets = at<int32_t>(ws, L.offsets);
 
   // 1. histogram, prefix sum + tile lists, stable scatter
@@ -189,13 +208,11 @@ int32_t forward_impl(const moe_dims* dims, int32_t T, const void* x, const int32
   p.inv = at<int32_t>(ws, L.inv);
   p.row_gate = at<float>(ws, L.row_gate);
   p.bm0 = moe::gemm_shape(fmt, 0, T).bm;
-  p.tiles0 = at<int2>(ws, L.tiles0);
-  p.n_tiles0 = ctrl + 0;
+  p.tile_off0 = at<int32_t>(ws, L.tile_off0);
   p.bm1 = moe::gemm_shape(fmt, 1, T).bm;
-  p.tiles1 = at<int2>(ws, L.tiles1);
-  p.n_tiles1 = ctrl + 1;
-  p.zero_words = amax_x;  // amax(x), amax(act)
-  p.n_zero = 2;
+  p.tile_off1 = at<int32_t>(ws, L.tile_off1);
+  p.zero_words = amax_x;  // amax slots of x and of the intermediate
+  p.n_zero = 2 * moe::kAmaxSlots;
   marks.mark(0);
   hipError_t err = moe::launch_permute(ids, gates, T, E, k, p, st);
   if (err != hipSuccess) return MOE_EHIP;
@@ -206,9 +223,9 @@ int32_t forward_impl(const moe_dims* dims, int32_t T, const void* x, const int32
   if (fmt == kFP8) {
     err = moe::launch_amax_bf16(static_cast<const uint16_t*>(x), nullptr, T, H, amax_x, st);
     if (err == hipSuccess)
-      err = moe::launch_quant_fp8(static_cast<const uint16_t*>(x), nullptr, T, H, amax_x,
-                                  at<uint8_t>(ws, L.x_q), scales + 0, st);
-    a_up = at<uint8_t>(ws, L.x_q);
+      err = moe::launch_quant_fp8(static_cast<const uint16_t*>(x), nullptr, T, H, amax_x, 0,
+                                  at<uint16_t>(ws, L.x_q), nullptr, scales + 0, st);
+    a_up = at<uint16_t>(ws, L.x_q);
   } else if (fmt == kNVFP4) {
     err = moe::launch_amax_bf16(static_cast<const uint16_t*>(x), nullptr, T, H, amax_x, st);
     if (err == hipSuccess)
@@ -221,8 +238,8 @@ int32_t forward_impl(const moe_dims* dims, int32_t T, const void* x, const int32
   // 3. grouped up projection + ReLU^2
   marks.mark(2);
   moe::GemmArgs g{};
-  g.tiles = p.tiles0;
-  g.n_tiles = p.n_tiles0;
+  g.tile_off = p.tile_off0;
+  g.E = E;
   g.max_tiles = (R + p.bm0 - 1) / p.bm0 + (R < E ? R : E);
   g.offsets = offsets;
   g.sorted_src = p.sorted_src;
@@ -244,7 +261,7 @@ int32_t forward_impl(const moe_dims* dims, int32_t T, const void* x, const int32
   marks.mark(3);
   const void* a_down = at<uint16_t>(ws, L.act);
   if (fmt == kFP8) {
-    err = moe::launch_quant_fp8(at<uint16_t>(ws, L.act), offsets + E, R, F, amax_a,
+    err = moe::launch_quant_fp8(at<uint16_t>(ws, L.act), offsets + E, R, F, amax_a, 1, nullptr,
                                 at<uint8_t>(ws, L.act_q), scales + 1, st);
     a_down = at<uint8_t>(ws, L.act_q);
   } else if (fmt == kNVFP4) {
@@ -255,8 +272,7 @@ int32_t forward_impl(const moe_dims* dims, int32_t T, const void* x, const int32
 
   // 5. grouped down projection, gate applied per row
   marks.mark(4);
-  g.tiles = p.tiles1;
-  g.n_tiles = p.n_tiles1;
+  g.tile_off = p.tile_off1;
   g.max_tiles = (R + p.bm1 - 1) / p.bm1 + (R < E ? R : E);
   g.sorted_src = nullptr;
   g.a = a_down;
@@ -326,14 +342,14 @@ int32_t moe_quantize_activation(int32_t fmt, int32_t rows, int32_t cols, const v
   if (!ws || ws_bytes < kAlign) return MOE_EWORKSPACE;
   if (rows == 0) return MOE_OK;
   const hipStream_t st = static_cast<hipStream_t>(stream);
-  uint32_t* amax = static_cast<uint32_t*>(ws);
-  hipError_t err = moe::launch_zero_u32(amax, 1, st);
+  uint32_t* amax = static_cast<uint32_t*>(ws);  // kAmaxSlots words
+  hipError_t err = moe::launch_zero_u32(amax, moe::kAmaxSlots, st);
   if (err == hipSuccess)
     err = moe::launch_amax_bf16(static_cast<const uint16_t*>(x), nullptr, rows, cols, amax, st);
   if (err == hipSuccess) {
     if (fmt == kFP8)
-      err = moe::launch_quant_fp8(static_cast<const uint16_t*>(x), nullptr, rows, cols, amax,
-                                  static_cast<uint8_t*>(codes), scale, st);
+      err = moe::launch_quant_fp8(static_cast<const uint16_t*>(x), nullptr, rows, cols, amax, 1,
+                                  nullptr, static_cast<uint8_t*>(codes), scale, st);
     else
       err = moe::launch_quant_nvfp4(static_cast<const uint16_t*>(x), nullptr, rows, cols, amax, 1,
                                     nullptr, static_cast<uint8_t*>(codes), bs, scale, st);

@@ -7,6 +7,7 @@
 namespace moe {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef int32_t i32x8 __attribute__((ext_vector_type(8)));
@@ -113,6 +114,32 @@ __device__ __forceinline__ float wave_sum(float v) {
 // non-negative floats order like their bit patterns
 __device__ __forceinline__ void atomic_max_nonneg(uint32_t* slot, float v) {
   atomicMax(slot, __float_as_uint(v));
+}
+
+// A tensor amax is accumulated into kAmaxSlots words (block b uses slot
+// b % kAmaxSlots) so that thousands of blocks do not serialise on one
+// address; readers take the max over the slots.
+constexpr int kAmaxSlots = 64;
+
+// max over the slots, computed by one wave (every lane gets the result)
+__device__ __forceinline__ float read_amax_slots(const uint32_t* slots) {
+  const int lane = threadIdx.x & 63;
+  float v = lane < kAmaxSlots ? __uint_as_float(slots[lane]) : 0.f;
+  return wave_max(v);
+}
+
+// block-wide max of a per-thread value, one atomic per block (blockDim.x <= 1024)
+__device__ __forceinline__ void block_amax_to_slots(float v, uint32_t* slots) {
+  __shared__ float part[16];
+  v = wave_max(v);
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  if (lane == 0) part[wave] = v;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    float m = 0.f;
+    for (int w = 0; w < static_cast<int>((blockDim.x + 63) / 64); ++w) m = fmaxf(m, part[w]);
+    atomic_max_nonneg(slots + (blockIdx.x % kAmaxSlots), m);
+  }
 }
 
 }  // namespace moe

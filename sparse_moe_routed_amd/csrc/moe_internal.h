@@ -7,6 +7,9 @@
 namespace moe {
 
 enum Fmt { kBF16 = 0, kFP8 = 1, kNVFP4 = 2 };
+// GEMM operand modes: kFP8 runs the FP8 MFMA on E4M3 codes; kFP8X expands
+// E4M3 weight codes to bf16 (exact) in LDS and runs the BF16 MFMA.
+constexpr int kFP8X = 3;
 
 constexpr int kChunk = 2048;  // flat (token, slot) entries per permutation chunk
 
@@ -19,17 +22,19 @@ struct PermBufs {
   int32_t* inv;           // [R]
   float* row_gate;        // [R]
   int bm0;                // rows per tile, list 0 (up projection)
-  int2* tiles0;
-  int32_t* n_tiles0;
+  int32_t* tile_off0;     // [E + 1]: exclusive prefix of ceil(count_e / bm0)
   int bm1;                // rows per tile, list 1 (down projection)
-  int2* tiles1;
-  int32_t* n_tiles1;
+  int32_t* tile_off1;     // [E + 1]
   uint32_t* zero_words;   // cleared by the scan (amax slots)
   int n_zero;
 };
 
-hipError_t launch_router(const uint16_t* x, const float* w, const float* bias, int T, int H,
-                         int E, int k, int32_t* ids, float* gates, hipStream_t stream);
+// K slices of the router GEMV for T tokens (partial logits [S, T, E] fp32)
+int router_k_slices(int T, int H);
+hipError_t launch_router_pack(const float* w, int E, int H, uint16_t* packed, hipStream_t stream);
+hipError_t launch_router(const uint16_t* x, const uint16_t* w_packed, const float* bias, int T,
+                         int H, int E, int k, float* part, int32_t* ids, float* gates,
+                         hipStream_t stream);
 
 hipError_t launch_permute(const int32_t* ids, const float* gates, int T, int E, int k,
                           const PermBufs& p, hipStream_t stream);
@@ -38,9 +43,9 @@ hipError_t launch_permute(const int32_t* ids, const float* gates, int T, int E, 
 // with A_g the token rows gathered through sorted_src; down:
 // out = fp32(gate * scale * A W^T).
 struct GemmArgs {
-  const int2* tiles;
-  const int32_t* n_tiles;
-  int max_tiles;
+  const int32_t* tile_off;    // [E + 1]: row tiles of experts < e (bm rows each)
+  int E;
+  int max_tiles;              // upper bound of tile_off[E] (grid sizing)
   const int32_t* offsets;     // [E + 1]
   const int32_t* sorted_src;  // up only: flat index of each sorted row
   int top_k;
@@ -68,10 +73,11 @@ hipError_t launch_gemm(int fmt, int stage, int T, const GemmArgs& g, hipStream_t
 // activation quantisers
 hipError_t launch_amax_bf16(const uint16_t* x, const int32_t* n_rows_dev, int rows, int cols,
                             uint32_t* amax, hipStream_t stream);
-// FP8: codes = E4M3(f32(x * f32(448/amax))); writes scale f32(amax/448) to *scale
+// FP8: codes = E4M3(f32(x * f32(448/amax))); writes scale f32(amax/448) to *scale.
+// mode 0: dec(code) as bf16 into deq; mode 1: the codes.
 hipError_t launch_quant_fp8(const uint16_t* x, const int32_t* n_rows_dev, int rows, int cols,
-                            const uint32_t* amax, uint8_t* codes, float* scale,
-                            hipStream_t stream);
+                            const uint32_t* amax, int mode, uint16_t* deq, uint8_t* codes,
+                            float* scale, hipStream_t stream);
 // NVFP4: per 16-block codes and E4M3 scale; writes tensor scale to *scale.
 // mode 0: dequantised block values dec(q)*dec(sb) as bf16 into deq (may alias x);
 // mode 1: packed codes + block scales.

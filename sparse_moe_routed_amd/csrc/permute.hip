@@ -1,5 +1,5 @@
 // Token permutation: per-expert histogram, exclusive prefix sum with a
-// device-side GEMM tile list, and a stable scatter of (token, slot) rows into
+// per-expert GEMM tile counts, and a stable scatter of (token, slot) rows into
 // expert-contiguous order.
 //
 // Grouped expert matrix multiplication needs the rows routed to one expert
@@ -10,8 +10,9 @@
 //
 // The flat ids are cut into chunks of kChunk entries.  perm_count writes
 // per-chunk expert counts; perm_scan (one workgroup) turns them into chunk
-// bases, expert offsets and the tile lists; perm_scatter recomputes each
-// entry's stable rank inside its chunk with wave ballots.  No host sync.
+// bases, expert offsets and per-expert row-tile prefixes for the GEMMs;
+// perm_scatter recomputes each entry's stable rank inside its chunk with wave
+// ballots.  No host sync.
 #include "moe_common.h"
 #include "moe_internal.h"
 
@@ -64,9 +65,8 @@ __device__ int block_exclusive_scan(int v, int* tmp, int& total) {
 __global__ __launch_bounds__(kPermThreads) void perm_scan_kernel(
     const int32_t* __restrict__ chunk_counts, int n_chunks, int E,
     int32_t* __restrict__ chunk_base, int32_t* __restrict__ counts,
-    int32_t* __restrict__ offsets, int bm0, int2* __restrict__ tiles0,
-    int32_t* __restrict__ n_tiles0, int bm1, int2* __restrict__ tiles1,
-    int32_t* __restrict__ n_tiles1, uint32_t* __restrict__ zero_words, int n_zero) {
+    int32_t* __restrict__ offsets, int bm0, int32_t* __restrict__ tile_off0, int bm1,
+    int32_t* __restrict__ tile_off1, uint32_t* __restrict__ zero_words, int n_zero) {
   __shared__ int tmp[kPermThreads / 64];
   const int e = threadIdx.x;
   for (int i = threadIdx.x; i < n_zero; i += kPermThreads) zero_words[i] = 0u;
@@ -84,17 +84,15 @@ __global__ __launch_bounds__(kPermThreads) void perm_scan_kernel(
   if (e < E) offsets[e] = off;
   if (e == 0) offsets[E] = total;
 
-  // tile lists: expert e owns ceil(count / bm) tiles of up to bm rows
+  // per-expert row-tile prefix: expert e owns ceil(count / bm) tiles of up to bm rows
   for (int list = 0; list < 2; ++list) {
     const int bm = list ? bm1 : bm0;
-    int2* tiles = list ? tiles1 : tiles0;
-    int32_t* n_tiles = list ? n_tiles1 : n_tiles0;
-    if (tiles == nullptr) continue;
+    int32_t* tile_off = list ? tile_off1 : tile_off0;
     const int nt = e < E ? (run + bm - 1) / bm : 0;
     int nt_total;
     const int tbase = block_exclusive_scan(nt, tmp, nt_total);
-    for (int i = 0; i < nt; ++i) tiles[tbase + i] = make_int2(e, off + i * bm);
-    if (e == 0) *n_tiles = nt_total;
+    if (e < E) tile_off[e] = tbase;
+    if (e == 0) tile_off[E] = nt_total;
   }
 }
 
@@ -164,8 +162,7 @@ hipError_t launch_permute(const int32_t* ids, const float* gates, int T, int E, 
                      E, p.chunk_counts);
   hipLaunchKernelGGL(perm_scan_kernel, dim3(1), dim3(kPermThreads), 0, stream,
                      p.chunk_counts, n_chunks, E, p.chunk_base, p.counts, p.offsets, p.bm0,
-                     p.tiles0, p.n_tiles0, p.bm1, p.tiles1, p.n_tiles1, p.zero_words,
-                     p.n_zero);
+                     p.tile_off0, p.bm1, p.tile_off1, p.zero_words, p.n_zero);
   hipLaunchKernelGGL(perm_scatter_kernel, dim3(n_chunks), dim3(kPermThreads), 0, stream, ids,
                      gates, R, E, k, p.chunk_base, p.offsets, p.sorted_src, p.inv, p.row_gate);
   return hipGetLastError();

@@ -19,16 +19,13 @@ namespace {
 
 constexpr int kQThreads = 256;
 
-__device__ __forceinline__ uint32_t load_amax_bits(const uint32_t* p) {
-  return __atomic_load_n(p, __ATOMIC_RELAXED);
-}
-
 __global__ __launch_bounds__(kQThreads) void zero_u32_kernel(uint32_t* p, int n) {
   const int i = blockIdx.x * kQThreads + threadIdx.x;
   if (i < n) p[i] = 0u;
 }
 
-// amax over rows [0, n_rows) of a bf16 [rows, cols] tensor; 8 elements per thread step
+// amax over rows [0, n_rows) of a bf16 [rows, cols] tensor into kAmaxSlots
+// slots; 8 elements per thread step
 __global__ __launch_bounds__(kQThreads) void amax_bf16_kernel(const uint16_t* __restrict__ x,
                                                               const int32_t* n_rows_dev, int rows,
                                                               int cols, uint32_t* amax) {
@@ -44,17 +41,18 @@ __global__ __launch_bounds__(kQThreads) void amax_bf16_kernel(const uint16_t* __
       m = fmaxf(m, fabsf(bf16_to_f32(v[w] >> 16)));
     }
   }
-  m = wave_max(m);
-  if ((threadIdx.x & 63) == 0) atomic_max_nonneg(amax, m);
+  block_amax_to_slots(m, amax);
 }
 
-// FP8: 16 elements per thread
+// FP8: 16 elements per thread.  mode 0 writes dec(code) as bf16 (exact) into
+// deq; mode 1 writes the codes.
 __global__ __launch_bounds__(kQThreads) void quant_fp8_kernel(const uint16_t* __restrict__ x,
                                                               const int32_t* n_rows_dev, int rows,
                                                               int cols, const uint32_t* amax_p,
+                                                              int mode, uint16_t* __restrict__ deq,
                                                               uint8_t* __restrict__ codes,
                                                               float* scale) {
-  const float amax = __uint_as_float(load_amax_bits(amax_p));
+  const float amax = read_amax_slots(amax_p);
   if (blockIdx.x == 0 && threadIdx.x == 0) *scale = amax > 0.f ? __fdiv_rn(amax, 448.f) : 0.f;
   const int nr = n_rows_dev ? min(*n_rows_dev, rows) : rows;
   const size_t n16 = static_cast<size_t>(nr) * cols / 16;
@@ -63,21 +61,30 @@ __global__ __launch_bounds__(kQThreads) void quant_fp8_kernel(const uint16_t* __
        i += static_cast<size_t>(gridDim.x) * kQThreads) {
     const u32x4 v0 = reinterpret_cast<const u32x4*>(x)[2 * i];
     const u32x4 v1 = reinterpret_cast<const u32x4*>(x)[2 * i + 1];
-    uint32_t out[4];
+    uint32_t q[16];
 #pragma unroll
     for (int w = 0; w < 4; ++w) {
-      const uint32_t a = w < 2 ? v0[2 * w] : v1[2 * (w - 2)];
-      const uint32_t b = w < 2 ? v0[2 * w + 1] : v1[2 * (w - 2) + 1];
-      uint32_t q0 = 0, q1 = 0, q2 = 0, q3 = 0;
-      if (amax > 0.f) {
-        q0 = e4m3_encode(bf16_to_f32(a & 0xffffu) * inv);
-        q1 = e4m3_encode(bf16_to_f32(a >> 16) * inv);
-        q2 = e4m3_encode(bf16_to_f32(b & 0xffffu) * inv);
-        q3 = e4m3_encode(bf16_to_f32(b >> 16) * inv);
-      }
-      out[w] = q0 | (q1 << 8) | (q2 << 16) | (q3 << 24);
+      const uint32_t a = v0[w], b = v1[w];
+      q[2 * w] = amax > 0.f ? e4m3_encode(bf16_to_f32(a & 0xffffu) * inv) : 0u;
+      q[2 * w + 1] = amax > 0.f ? e4m3_encode(bf16_to_f32(a >> 16) * inv) : 0u;
+      q[8 + 2 * w] = amax > 0.f ? e4m3_encode(bf16_to_f32(b & 0xffffu) * inv) : 0u;
+      q[8 + 2 * w + 1] = amax > 0.f ? e4m3_encode(bf16_to_f32(b >> 16) * inv) : 0u;
     }
-    reinterpret_cast<u32x4*>(codes)[i] = u32x4{out[0], out[1], out[2], out[3]};
+    if (mode == 0) {
+      uint32_t o[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j)
+        o[j] = (__float_as_uint(e4m3_decode(q[2 * j])) >> 16) |
+               (__float_as_uint(e4m3_decode(q[2 * j + 1])) & 0xffff0000u);
+      reinterpret_cast<u32x4*>(deq)[2 * i] = u32x4{o[0], o[1], o[2], o[3]};
+      reinterpret_cast<u32x4*>(deq)[2 * i + 1] = u32x4{o[4], o[5], o[6], o[7]};
+    } else {
+      uint32_t out[4];
+#pragma unroll
+      for (int w = 0; w < 4; ++w)
+        out[w] = q[4 * w] | (q[4 * w + 1] << 8) | (q[4 * w + 2] << 16) | (q[4 * w + 3] << 24);
+      reinterpret_cast<u32x4*>(codes)[i] = u32x4{out[0], out[1], out[2], out[3]};
+    }
   }
 }
 
@@ -88,7 +95,7 @@ __global__ __launch_bounds__(kQThreads) void quant_nvfp4_kernel(
     const uint16_t* x, const int32_t* n_rows_dev, int rows, int cols, const uint32_t* amax_p,
     int mode, uint16_t* deq, uint8_t* __restrict__ codes, uint8_t* __restrict__ bs,
     float* scale) {
-  const float amax = __uint_as_float(load_amax_bits(amax_p));
+  const float amax = read_amax_slots(amax_p);
   const float S = amax > 0.f ? __fdiv_rn(amax, 2688.f) : 0.f;
   if (blockIdx.x == 0 && threadIdx.x == 0 && scale) *scale = S;
   const float sixS = 6.f * S;
@@ -264,18 +271,18 @@ hipError_t launch_zero_u32(uint32_t* p, int n, hipStream_t stream) {
 
 hipError_t launch_amax_bf16(const uint16_t* x, const int32_t* n_rows_dev, int rows, int cols,
                             uint32_t* amax, hipStream_t stream) {
-  const int grid = grid_for(static_cast<size_t>(rows) * cols / 8, 2048);
+  const int grid = grid_for(static_cast<size_t>(rows) * cols / 8, 1024);
   hipLaunchKernelGGL(amax_bf16_kernel, dim3(grid), dim3(kQThreads), 0, stream, x, n_rows_dev,
                      rows, cols, amax);
   return hipGetLastError();
 }
 
 hipError_t launch_quant_fp8(const uint16_t* x, const int32_t* n_rows_dev, int rows, int cols,
-                            const uint32_t* amax, uint8_t* codes, float* scale,
-                            hipStream_t stream) {
+                            const uint32_t* amax, int mode, uint16_t* deq, uint8_t* codes,
+                            float* scale, hipStream_t stream) {
   const int grid = grid_for(static_cast<size_t>(rows) * cols / 16, 4096);
   hipLaunchKernelGGL(quant_fp8_kernel, dim3(grid), dim3(kQThreads), 0, stream, x, n_rows_dev,
-                     rows, cols, amax, codes, scale);
+                     rows, cols, amax, mode, deq, codes, scale);
   return hipGetLastError();
 }
 

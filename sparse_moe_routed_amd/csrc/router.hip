@@ -6,14 +6,18 @@
 // execution (audio.cpp notes "NVIDIA Nemotron 3.5 Transcribe", section "CPU
 // weight offload").
 //
-// The logits are a dense [T, H] x [H, E] contraction, so they run on MFMA:
-// each fp32 router weight w is split exactly into three bf16 parts
-// (hi + mid + lo == w), and x is bf16, so every product x * part is exact in
-// the fp32 accumulator of v_mfma_f32_16x16x32_bf16.  A workgroup owns 16
-// tokens and all experts; its logits stay in LDS for the selection.  Its 16
-// waves split the work as 8 expert blocks x 2 halves of K, and each wave keeps
-// four K steps of loads in flight (the router matrix is re-read from L2 by
-// every workgroup, so the loop is latency-bound, not bandwidth-bound).
+// The logits are a dense [T, H] x [H, E] contraction, so they run on MFMA.
+// The fp32 router matrix is packed once (router_pack_kernel) into three bf16
+// matrices with w == hi + mid + lo exactly; x is bf16, so every product
+// x * part is exact in the fp32 accumulator of v_mfma_f32_16x16x32_bf16 and
+// the logits carry only fp32 summation error.
+//
+// router_logits_kernel: a workgroup computes 64 tokens against 16 (small
+// batches) or 64 experts over one of S slices of K (S > 1 spreads small
+// batches over more CUs); waves keep several K steps of loads in flight.
+// Partial logits go to the workspace as [S, T, E] fp32.
+// router_topk_kernel: one wave per token sums the S partials in order, adds
+// the bias, selects the top k (ties to the lower index) and writes the gates.
 #include "moe_common.h"
 #include "moe_internal.h"
 
@@ -21,134 +25,159 @@ namespace moe {
 
 namespace {
 
-constexpr int kTokTile = 16;   // tokens per workgroup (MFMA M)
-constexpr int kRouterThreads = 1024;
-constexpr int kKParts = 2;       // K halves per expert block
-constexpr int kEBlkPar = 8;      // expert blocks processed side by side
+constexpr int kTokPerWave = 16;
+constexpr int kWavesPerWg = 4;
+constexpr int kTokPerWg = kTokPerWave * kWavesPerWg;
 constexpr int kMaxE = 256;
 
-// exact split of an fp32 value into three bf16 values (truncations; the
-// residual after two truncations has at most 8 significant bits)
-__device__ __forceinline__ void split3(float w, __bf16& hi, __bf16& mid, __bf16& lo) {
-  const uint32_t u = __float_as_uint(w);
-  const float h = __uint_as_float(u & 0xffff0000u);
-  const float r1 = w - h;
-  const float m = __uint_as_float(__float_as_uint(r1) & 0xffff0000u);
-  const float r2 = r1 - m;
-  hi = __builtin_bit_cast(__bf16, static_cast<uint16_t>(u >> 16));
-  mid = __builtin_bit_cast(__bf16, static_cast<uint16_t>(__float_as_uint(m) >> 16));
-  lo = __builtin_bit_cast(__bf16, f32_to_bf16(r2));
+__global__ __launch_bounds__(256) void router_pack_kernel(const float* __restrict__ w, size_t n,
+                                                          uint16_t* __restrict__ packed) {
+  for (size_t i = static_cast<size_t>(blockIdx.x) * 256 + threadIdx.x; i < n;
+       i += static_cast<size_t>(gridDim.x) * 256) {
+    const float v = w[i];
+    const uint32_t u = __float_as_uint(v);
+    const float hi = __uint_as_float(u & 0xffff0000u);  // truncation: exact residual
+    const float r1 = v - hi;
+    const float mid = __uint_as_float(__float_as_uint(r1) & 0xffff0000u);
+    const float r2 = r1 - mid;  // at most 8 significant bits: exact in bf16
+    packed[i] = static_cast<uint16_t>(u >> 16);
+    packed[n + i] = static_cast<uint16_t>(__float_as_uint(mid) >> 16);
+    packed[2 * n + i] = f32_to_bf16(r2);
+  }
 }
 
-__global__ __launch_bounds__(kRouterThreads) void router_topk_kernel(
-    const uint16_t* __restrict__ x, const float* __restrict__ w,
-    const float* __restrict__ bias, int T, int H, int E, int k,
-    int32_t* __restrict__ ids, float* __restrict__ gates) {
-  __shared__ float logits[kKParts][kTokTile][kMaxE + 1];
+// TB = 16-token row blocks per wave.  TB == 1 (small batches): the 4 waves
+// take 4 row blocks of one 16-expert block.  TB == 4: each wave takes all 64
+// tokens of the workgroup against its own 16-expert block, reusing every
+// router fragment for 4 MFMA row blocks (less L2 traffic per logit).
+template <int TB>
+__global__ __launch_bounds__(256) void router_logits_kernel(const uint16_t* __restrict__ x,
+                                                            const uint16_t* __restrict__ wp,
+                                                            int T, int H, int E, int S,
+                                                            float* __restrict__ part) {
+  constexpr int U = TB == 1 ? 4 : 2;  // K steps of loads in flight
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
-  const int t0 = blockIdx.x * kTokTile;
-  const int row = lane & 15;         // MFMA row (token) / column (expert) of this lane
-  const int kq = (lane >> 4) * 8;    // this lane's 8-wide K slice inside a 32-K step
-  const int tok = min(t0 + row, T - 1);
-  const uint16_t* xrow = x + static_cast<size_t>(tok) * H + kq;
-  const int n_eblk = E / 16;
-  const int kp = wave / kEBlkPar;
-  const int kbeg = kp * (H / kKParts), kend = kbeg + H / kKParts;
+  const int t0 = blockIdx.x * kTokPerWg + (TB == 1 ? wave * kTokPerWave : 0);
+  const int eb = TB == 1 ? blockIdx.y : blockIdx.y * kWavesPerWg + wave;
+  if (t0 >= T || eb * 16 >= E) return;  // no barriers in this kernel
+  const int s = blockIdx.z;
+  const int row = lane & 15;       // MFMA row (token) / column (expert) of this lane
+  const int kq = (lane >> 4) * 8;  // this lane's 8-wide K slice inside a 32-K step
+  const int kbeg = s * (H / S), kend = kbeg + H / S;
+  const size_t n = static_cast<size_t>(E) * H;
+  const uint16_t* xrow[TB];
+#pragma unroll
+  for (int b = 0; b < TB; ++b)
+    xrow[b] = x + static_cast<size_t>(min(t0 + b * 16 + row, T - 1)) * H + kq;
+  const uint16_t* w_hi = wp + static_cast<size_t>(eb * 16 + row) * H + kq;
+  const uint16_t* w_mid = w_hi + n;
+  const uint16_t* w_lo = w_hi + 2 * n;
 
-  for (int eb = wave % kEBlkPar; eb < n_eblk; eb += kEBlkPar) {
-    const float* wrow = w + static_cast<size_t>(eb * 16 + row) * H + kq;
-    f32x4 acc[4];
+  f32x4 acc[TB][U];
 #pragma unroll
-    for (int u = 0; u < 4; ++u) acc[u] = f32x4{0.f, 0.f, 0.f, 0.f};
-    for (int k0 = kbeg; k0 < kend; k0 += 4 * 32) {
-      bf16x8 a[4];
-      f32x4 w0[4], w1[4];
+  for (int b = 0; b < TB; ++b)
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {  // issue the loads of four K steps first
-        const int kk = k0 + u * 32;
-        if (kk < kend) {
-          a[u] = *reinterpret_cast<const bf16x8*>(xrow + kk);
-          w0[u] = *reinterpret_cast<const f32x4*>(wrow + kk);
-          w1[u] = *reinterpret_cast<const f32x4*>(wrow + kk + 4);
-        }
-      }
+    for (int u = 0; u < U; ++u) acc[b][u] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int k0 = kbeg; k0 < kend; k0 += U * 32) {
+    bf16x8 a[U][TB], bh[U], bm[U], bl[U];
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        if (k0 + u * 32 >= kend) break;
-        bf16x8 bh, bm, bl;
+    for (int u = 0; u < U; ++u) {  // issue the loads of U K steps first
+      const int kk = k0 + u * 32;
+      if (kk < kend) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          __bf16 h0, m0, l0, h1, m1, l1;
-          split3(w0[u][i], h0, m0, l0);
-          split3(w1[u][i], h1, m1, l1);
-          bh[i] = h0; bm[i] = m0; bl[i] = l0;
-          bh[i + 4] = h1; bm[i + 4] = m1; bl[i + 4] = l1;
-        }
-        acc[u] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[u], bl, acc[u], 0, 0, 0);
-        acc[u] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[u], bm, acc[u], 0, 0, 0);
-        acc[u] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[u], bh, acc[u], 0, 0, 0);
+        for (int b = 0; b < TB; ++b) a[u][b] = *reinterpret_cast<const bf16x8*>(xrow[b] + kk);
+        bh[u] = *reinterpret_cast<const bf16x8*>(w_hi + kk);
+        bm[u] = *reinterpret_cast<const bf16x8*>(w_mid + kk);
+        bl[u] = *reinterpret_cast<const bf16x8*>(w_lo + kk);
       }
     }
-    // 16x16 f32 result: lane holds column (expert) lane%16, rows 4*(lane/16)+r
-    const int e = eb * 16 + row;
 #pragma unroll
-    for (int r = 0; r < 4; ++r)
-      logits[kp][(lane >> 4) * 4 + r][e] = (acc[0][r] + acc[1][r]) + (acc[2][r] + acc[3][r]);
+    for (int u = 0; u < U; ++u) {
+      if (k0 + u * 32 >= kend) break;
+#pragma unroll
+      for (int b = 0; b < TB; ++b) {
+        acc[b][u] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[u][b], bl[u], acc[b][u], 0, 0, 0);
+        acc[b][u] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[u][b], bm[u], acc[b][u], 0, 0, 0);
+        acc[b][u] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[u][b], bh[u], acc[b][u], 0, 0, 0);
+      }
+    }
   }
-  __syncthreads();
+  // 16x16 f32 result: lane holds column (expert) lane%16, rows 4*(lane/16)+r
+  const int e = eb * 16 + row;
+#pragma unroll
+  for (int b = 0; b < TB; ++b) {
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int t = t0 + b * 16 + (lane >> 4) * 4 + r;
+      float v = 0.f;
+#pragma unroll
+      for (int u = 0; u < U; ++u) v += acc[b][u][r];
+      if (t < T) part[(static_cast<size_t>(s) * T + t) * E + e] = v;
+    }
+  }
+}
 
-  // top-k: one token per wave; a lane holds experts lane + 64 i
-  for (int tt = wave; tt < kTokTile; tt += kRouterThreads / 64) {
-    const int t = t0 + tt;
-    if (t >= T) break;
-    float v[kMaxE / 64];
+__global__ __launch_bounds__(256) void router_topk_kernel(const float* __restrict__ part,
+                                                          const float* __restrict__ bias, int T,
+                                                          int E, int S, int k,
+                                                          int32_t* __restrict__ ids,
+                                                          float* __restrict__ gates) {
+  const int lane = threadIdx.x & 63;
+  const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (t >= T) return;
+  float v[kMaxE / 64];
+#pragma unroll
+  for (int i = 0; i < kMaxE / 64; ++i) {
+    const int e = lane + 64 * i;
+    if (e < E) {
+      float l = 0.f;
+      for (int s = 0; s < S; ++s) l += part[(static_cast<size_t>(s) * T + t) * E + e];
+      v[i] = l + (bias ? bias[e] : 0.f);
+    } else {
+      v[i] = -INFINITY;
+    }
+  }
+  float sel_v[8];
+  int sel_i[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    sel_v[j] = 0.f;
+    sel_i[j] = 0;
+    if (j >= k) continue;
+    float bv = -INFINITY;
+    int bi = 0x7fffffff;
 #pragma unroll
     for (int i = 0; i < kMaxE / 64; ++i) {
       const int e = lane + 64 * i;
-      v[i] = e < E ? (logits[0][tt][e] + logits[1][tt][e]) + (bias ? bias[e] : 0.f) : -INFINITY;
+      if (e < E && (v[i] > bv || (v[i] == bv && e < bi))) { bv = v[i]; bi = e; }
     }
-    float sel_v[8];
-    int sel_i[8];
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) {
+      const float ov = __shfl_xor(bv, o);
+      const int oi = __shfl_xor(bi, o);
+      if (ov > bv || (ov == bv && oi < bi)) { bv = ov; bi = oi; }
+    }
+    sel_v[j] = bv;
+    sel_i[j] = bi;
+#pragma unroll
+    for (int i = 0; i < kMaxE / 64; ++i)
+      if (lane + 64 * i == bi) v[i] = -INFINITY;  // remove the winner
+  }
+  if (lane == 0) {
+    const float m = sel_v[0];
+    float z[8];
+    float sum = 0.f;
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
-      sel_v[j] = 0.f;
-      sel_i[j] = 0;
-      if (j >= k) continue;
-      float bv = -INFINITY;
-      int bi = 0x7fffffff;
-#pragma unroll
-      for (int i = 0; i < kMaxE / 64; ++i) {
-        const int e = lane + 64 * i;
-        if (e < E && (v[i] > bv || (v[i] == bv && e < bi))) { bv = v[i]; bi = e; }
-      }
-#pragma unroll
-      for (int o = 32; o > 0; o >>= 1) {
-        const float ov = __shfl_xor(bv, o);
-        const int oi = __shfl_xor(bi, o);
-        if (ov > bv || (ov == bv && oi < bi)) { bv = ov; bi = oi; }
-      }
-      sel_v[j] = bv;
-      sel_i[j] = bi;
-#pragma unroll
-      for (int i = 0; i < kMaxE / 64; ++i)
-        if (lane + 64 * i == bi) v[i] = -INFINITY;  // remove the winner
+      z[j] = j < k ? expf(sel_v[j] - m) : 0.f;
+      sum += z[j];
     }
-    if (lane == 0) {
-      const float m = sel_v[0];
-      float z[8];
-      float sum = 0.f;
 #pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        z[j] = j < k ? expf(sel_v[j] - m) : 0.f;
-        sum += z[j];
-      }
-#pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        if (j < k) {
-          ids[static_cast<size_t>(t) * k + j] = sel_i[j];
-          gates[static_cast<size_t>(t) * k + j] = z[j] / sum;
-        }
+    for (int j = 0; j < 8; ++j) {
+      if (j < k) {
+        ids[static_cast<size_t>(t) * k + j] = sel_i[j];
+        gates[static_cast<size_t>(t) * k + j] = z[j] / sum;
       }
     }
   }
@@ -156,12 +185,38 @@ __global__ __launch_bounds__(kRouterThreads) void router_topk_kernel(
 
 }  // namespace
 
-hipError_t launch_router(const uint16_t* x, const float* w, const float* bias, int T,
-                         int H, int E, int k, int32_t* ids, float* gates,
+// K slices: each wave's K loop is a chain of L2 round trips, so the router
+// splits K four ways at every batch size (more waves in flight, shorter chains)
+int router_k_slices(int /*T*/, int H) {
+  int S = 4;
+  while (S > 1 && H % (32 * S)) S >>= 1;
+  return S;
+}
+
+hipError_t launch_router_pack(const float* w, int E, int H, uint16_t* packed, hipStream_t stream) {
+  const size_t n = static_cast<size_t>(E) * H;
+  size_t g = (n + 255) / 256;
+  if (g > 4096) g = 4096;
+  hipLaunchKernelGGL(router_pack_kernel, dim3(static_cast<unsigned>(g)), dim3(256), 0, stream, w,
+                     n, packed);
+  return hipGetLastError();
+}
+
+hipError_t launch_router(const uint16_t* x, const uint16_t* w_packed, const float* bias, int T,
+                         int H, int E, int k, float* part, int32_t* ids, float* gates,
                          hipStream_t stream) {
-  const int blocks = (T + kTokTile - 1) / kTokTile;
-  hipLaunchKernelGGL(router_topk_kernel, dim3(blocks), dim3(kRouterThreads), 0, stream,
-                     x, w, bias, T, H, E, k, ids, gates);
+  const int S = router_k_slices(T, H);
+  if (T <= 256) {
+    const dim3 grid((T + kTokPerWg - 1) / kTokPerWg, E / 16, S);
+    hipLaunchKernelGGL(router_logits_kernel<1>, grid, dim3(256), 0, stream, x, w_packed, T, H, E,
+                       S, part);
+  } else {
+    const dim3 grid((T + kTokPerWg - 1) / kTokPerWg, (E / 16 + kWavesPerWg - 1) / kWavesPerWg, S);
+    hipLaunchKernelGGL(router_logits_kernel<4>, grid, dim3(256), 0, stream, x, w_packed, T, H, E,
+                       S, part);
+  }
+  hipLaunchKernelGGL(router_topk_kernel, dim3((T + 3) / 4), dim3(256), 0, stream, part, bias, T, E,
+                     S, k, ids, gates);
   return hipGetLastError();
 }
 

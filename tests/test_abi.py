@@ -86,19 +86,33 @@ def test_route_validation(lib):
     d = _dims()
     r = moe.Router(FAKE.value, None)
     st = None
-    assert lib.moe_route(None, 4, FAKE, ctypes.byref(r), FAKE, FAKE, st) == moe.EINVAL
-    assert lib.moe_route(ctypes.byref(d), -1, FAKE, ctypes.byref(r), FAKE, FAKE, st) == moe.EINVAL
-    assert lib.moe_route(ctypes.byref(d), 4, None, ctypes.byref(r), FAKE, FAKE, st) == moe.EINVAL
-    assert lib.moe_route(ctypes.byref(d), 4, FAKE, None, FAKE, FAKE, st) == moe.EINVAL
-    r0 = moe.Router(None, None)
-    assert lib.moe_route(ctypes.byref(d), 4, FAKE, ctypes.byref(r0), FAKE, FAKE, st) == moe.EINVAL
-    assert lib.moe_route(ctypes.byref(_dims(k=0)), 4, FAKE, ctypes.byref(r), FAKE, FAKE, st) == moe.EINVAL
-    assert lib.moe_route(ctypes.byref(_dims(e=8, k=9)), 4, FAKE, ctypes.byref(r), FAKE, FAKE, st) == moe.EINVAL
-    assert lib.moe_route(ctypes.byref(_dims(k=9)), 4, FAKE, ctypes.byref(r), FAKE, FAKE, st) == moe.EUNSUPPORTED
-    assert lib.moe_route(ctypes.byref(_dims(e=120)), 4, FAKE, ctypes.byref(r), FAKE, FAKE, st) == moe.EUNSUPPORTED
-    assert lib.moe_route(ctypes.byref(_dims(h=2690)), 4, FAKE, ctypes.byref(r), FAKE, FAKE, st) == moe.EUNSUPPORTED
+    need = lib.moe_route_workspace_size(ctypes.byref(d), 4)
+    assert need >= 4 * 128 * 4 and need % 256 == 0
+
+    def call(dims=d, T=4, x=FAKE, router=r, ids=FAKE, gates=FAKE, ws=FAKE, wsb=need):
+        return lib.moe_route(dims if dims is None else ctypes.byref(dims), T, x,
+                             router if router is None else ctypes.byref(router), ids, gates, ws,
+                             wsb, st)
+
+    assert call(dims=None) == moe.EINVAL
+    assert call(T=-1) == moe.EINVAL
+    assert call(x=None) == moe.EINVAL
+    assert call(router=None) == moe.EINVAL
+    assert call(router=moe.Router(None, None)) == moe.EINVAL
+    assert call(ids=None) == moe.EINVAL
+    assert call(dims=_dims(k=0)) == moe.EINVAL
+    assert call(dims=_dims(e=8, k=9)) == moe.EINVAL
+    assert call(dims=_dims(k=9)) == moe.EUNSUPPORTED
+    assert call(dims=_dims(e=120)) == moe.EUNSUPPORTED
+    assert call(dims=_dims(h=2690)) == moe.EUNSUPPORTED
+    assert call(ws=None) == moe.EWORKSPACE
+    assert call(wsb=64) == moe.EWORKSPACE
+    assert call(ws=ctypes.c_void_p(FAKE.value + 4)) == moe.EWORKSPACE
     # T == 0 is a no-op that touches nothing
-    assert lib.moe_route(ctypes.byref(d), 0, FAKE, ctypes.byref(r), FAKE, FAKE, st) == moe.OK
+    assert call(T=0, x=None, ids=None, gates=None, ws=None, wsb=0) == moe.OK
+    assert lib.moe_router_pack(ctypes.byref(d), None, FAKE, st) == moe.EINVAL
+    assert lib.moe_router_pack(None, FAKE, FAKE, st) == moe.EINVAL
+    assert lib.moe_route_workspace_size(None, 4) == 0
 
 
 def test_forward_validation(lib):

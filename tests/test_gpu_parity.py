@@ -36,8 +36,7 @@ class Layer:
         self.dims = dims
         self.w_r, self.b = synth.make_router(layer, dims)
         self.up, self.down = synth.make_experts(layer, dims)
-        self.w_r_d = self.w_r.cuda()
-        self.b_d = self.b.cuda()
+        self.router = moe.pack_router(self.w_r.cuda(), self.b.cuda(), _ld(dims))
         self.up_d = self.up.cuda()
         self.down_d = self.down.cuda()
         self._banks = {}
@@ -73,7 +72,7 @@ def _rel_err(y_gpu, y_ref):
 
 def _route_both(L, x):
     ids_o, g_o, gap, _ = om.route(x.float().numpy(), L.w_r.numpy(), L.b.numpy(), L.dims.top_k)
-    ids_g, g_g = moe.route(x.cuda(), L.w_r_d, L.b_d, _ld(L.dims))
+    ids_g, g_g = moe.route(x.cuda(), L.router, _ld(L.dims))
     torch.cuda.synchronize()
     return ids_o, g_o, gap, ids_g.cpu().numpy(), g_g.cpu().numpy()
 
@@ -192,7 +191,7 @@ def test_forward_quantised_full_shape(full, fmt, T):
 def test_forward_bf16_output_and_determinism(full):
     T = 64
     x = _x(T, FULL).cuda()
-    ids, g = moe.route(x, full.w_r_d, full.b_d)
+    ids, g = moe.route(x, full.router)
     y1 = moe.forward(x, ids, g, full.bank("bf16"))
     y2 = moe.forward(x, ids, g, full.bank("bf16"))
     yb = moe.forward(x, ids, g, full.bank("bf16"), y_dtype=torch.bfloat16)
@@ -203,7 +202,7 @@ def test_forward_bf16_output_and_determinism(full):
 
 def test_forward_empty_and_single(full):
     x = _x(1, FULL).cuda()
-    ids, g = moe.route(x, full.w_r_d, full.b_d)
+    ids, g = moe.route(x, full.router)
     y = moe.forward(x, ids, g, full.bank("bf16"))
     y0 = moe.forward(x[:0], ids[:0], g[:0], full.bank("bf16"))
     torch.cuda.synchronize()
@@ -233,7 +232,7 @@ def test_prefill_t4096_sampled_tokens(full):
     T = 4096
     x = _x(T, FULL, outliers=True)
     xd = x.cuda()
-    ids_g, g_g = moe.route(xd, full.w_r_d, full.b_d)
+    ids_g, g_g = moe.route(xd, full.router)
     y = moe.forward(xd, ids_g, g_g, full.bank("bf16"))
     torch.cuda.synchronize()
     rng = np.random.default_rng(0)
@@ -318,7 +317,7 @@ def test_stacked_small_shape_nvfp4():
     for l in range(n_layers):
         L = Layer(dims, l)
         xin = moe.prenorm(xg)
-        ids, g = moe.route(xin, L.w_r_d, L.b_d, _ld(dims))
+        ids, g = moe.route(xin, L.router, _ld(dims))
         y = moe.forward(xin, ids, g, L.bank("nvfp4"), _ld(dims))
         moe.residual_add(xg, y)
         xin_o = om.prenorm(xo)
