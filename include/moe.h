@@ -171,9 +171,10 @@ typedef struct {
   int64_t inv;        /* int32 [T*k]: sorted row of each flat index, -1 = dropped */
   int64_t act;        /* bf16 [T*k, F]: a = bf16(relu(h)^2), sorted row order */
   int64_t out_rows;   /* fp32 [T*k, H]: gate * W_down a~, sorted row order   */
-  int64_t x_q;        /* bf16 [T, H] dequantised token values without the
-                         tensor scale: FP8 dec(q); NVFP4 dec(q)*dec(sb)      */
-  int64_t act_q;      /* FP8: u8 [T*k, F] codes; NVFP4: in place over act    */
+  int64_t x_q;        /* [T, H] dequantised token values without the tensor
+                         scale: FP8 bf16 dec(q); NVFP4 fp16 dec(q)*dec(sb)   */
+  int64_t act_q;      /* FP8: u8 [T*k, F] codes; NVFP4: fp16 dec(q)*dec(sb)
+                         in place over act                                   */
   int64_t scales;     /* fp32 [2]: x scale, act scale                        */
   int64_t total;      /* bytes                                               */
 } moe_ws_layout;

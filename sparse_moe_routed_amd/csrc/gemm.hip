@@ -26,10 +26,12 @@
 //          significand (about 13 bits below the largest product), and the up
 //          projection's output is re-quantised, so that error would move
 //          intermediate E4M3 codes; exact products with fp32 sums do not.
-//   NVFP4: E2M1 codes expanded with v_cvt_scalef32_pk_bf16_fp4 (unit scale)
-//          and multiplied by the E4M3 block scale in fp32 (code * block scale
-//          has at most 6 significant bits, so the bf16 value is exact), then
-//          the BF16 MFMA; the two fp32 tensor scales are applied in the
+//   NVFP4: E2M1 codes expanded to fp16 with v_cvt_scalef32_pk_f16_fp4 (unit
+//          scale) and multiplied by the E4M3 block scale with v_pk_mul_f16:
+//          code * block scale has at most 6 significant bits and lies in
+//          [2^-10, 2688], so every fp16 value is exact; activations arrive as
+//          the same exact fp16 products.  Then v_mfma_f32_32x32x16_f16 (exact
+//          products, fp32 sums); the two fp32 tensor scales are applied in the
 //          epilogue.
 // Epilogues: up writes bf16(relu(h)^2) (and the tensor amax for quantised
 // formats); down writes fp32 gate * h per sorted row.
@@ -43,6 +45,14 @@ namespace moe {
 namespace {
 
 constexpr int kStepBytes = 128;  // K bytes of each A/B row staged per step
+#ifndef MOE_PREFETCH
+#define MOE_PREFETCH 2
+#endif
+constexpr int kPrefetch = MOE_PREFETCH;  // K steps of loads in flight per thread
+static_assert(kPrefetch == 2 || kPrefetch == 3, "prefetch depth");
+#ifndef MOE_SCHED
+#define MOE_SCHED 1
+#endif
 constexpr int kLds = 144;        // padded LDS row stride in bytes
 
 template <int FMT, int STAGE, int BM, int BN, int WM, int WN>
@@ -150,9 +160,9 @@ __global__ __launch_bounds__(WM* WN * 64) void grouped_gemm_kernel(GemmArgs g) {
 
   // two register sets: the loads of steps s+1 and s+2 are in flight while
   // step s is multiplied out of LDS
-  u32x4 a_reg[2][A_CH];
-  u32x4 b_reg[2][B_CH];
-  uint32_t s_reg[2][B_CH];
+  u32x4 a_reg[kPrefetch][A_CH];
+  u32x4 b_reg[kPrefetch][B_CH];
+  uint32_t s_reg[kPrefetch][B_CH];
 
   // Loads are issued unconditionally (no branches around vector memory ops,
   // so the compiler can wait for exactly the set it needs): steps past the end
@@ -199,26 +209,23 @@ __global__ __launch_bounds__(WM* WN * 64) void grouped_gemm_kernel(GemmArgs g) {
     for (int i = 0; i < B_CH; ++i) {
       if constexpr (FMT == kNVFP4) {
         // 32 E2M1 codes (element 2j in the low nibble of byte j), two block scales
-        const float sc0 = e4m3_decode(s_reg[SET][i] & 0xffu);
-        const float sc1 = e4m3_decode((s_reg[SET][i] >> 8) & 0xffu);
+        const _Float16 sc0 = static_cast<_Float16>(e4m3_decode(s_reg[SET][i] & 0xffu));
+        const _Float16 sc1 = static_cast<_Float16>(e4m3_decode((s_reg[SET][i] >> 8) & 0xffu));
         uint32_t outw[16];
 #pragma unroll
         for (int w = 0; w < 4; ++w) {
           const uint32_t word = b_reg[SET][i][w];
-          const float sc = w < 2 ? sc0 : sc1;
-          // two E2M1 values per byte as bf16 (unit scale: exact), times the block scale
-          bf16x2 p[4];
-          p[0] = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(word, 1.0f, 0);
-          p[1] = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(word, 1.0f, 1);
-          p[2] = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(word, 1.0f, 2);
-          p[3] = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(word, 1.0f, 3);
-#pragma unroll
-          for (int bb = 0; bb < 4; ++bb) {
-            const uint32_t pw = __builtin_bit_cast(uint32_t, p[bb]);
-            const float v0 = __uint_as_float(pw << 16) * sc;
-            const float v1 = __uint_as_float(pw & 0xffff0000u) * sc;
-            outw[w * 4 + bb] = (__float_as_uint(v0) >> 16) | (__float_as_uint(v1) & 0xffff0000u);
-          }
+          const _Float16 sc = w < 2 ? sc0 : sc1;
+          const f16x2 s2 = {sc, sc};
+          // two E2M1 values per byte as fp16 (unit scale), times the block scale
+          const f16x2 p0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(word, 1.0f, 0) * s2;
+          const f16x2 p1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(word, 1.0f, 1) * s2;
+          const f16x2 p2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(word, 1.0f, 2) * s2;
+          const f16x2 p3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(word, 1.0f, 3) * s2;
+          outw[w * 4 + 0] = __builtin_bit_cast(uint32_t, p0);
+          outw[w * 4 + 1] = __builtin_bit_cast(uint32_t, p1);
+          outw[w * 4 + 2] = __builtin_bit_cast(uint32_t, p2);
+          outw[w * 4 + 3] = __builtin_bit_cast(uint32_t, p3);
         }
         u32x4* dst = reinterpret_cast<u32x4*>(B + b_dst[i]);
 #pragma unroll
@@ -243,12 +250,20 @@ __global__ __launch_bounds__(WM* WN * 64) void grouped_gemm_kernel(GemmArgs g) {
     }
   };
 
-  // ---- which MFMA blocks of this wave hold live rows / columns (the epilogue
-  // stores only those; the main loop multiplies every block without branches,
-  // dead rows and columns hold clamped copies of live ones)
-  bool m_live[MB], n_live[NB];
-#pragma unroll
-  for (int i = 0; i < MB; ++i) m_live[i] = wm * WTM + i * 32 < rows_valid;
+  // ---- which MFMA blocks of this wave hold live rows / columns.  Row blocks
+  // past the expert's last row are skipped: the main loop is specialised on
+  // the number of live 32-row blocks of the wave (a wave-uniform value), so the
+  // padding of ragged experts costs no MFMA issue and no branches in the loop.
+  // Dead columns (past N) hold clamped copies of live ones and are only masked
+  // in the epilogue.
+  // Row blocks are dealt to the WM wave rows in turn (wave row wm owns 32-row
+  // blocks wm, wm + WM, ...), so a ragged tile's live blocks spread evenly
+  // over the waves, and waves sharing a SIMD get equal work.
+  const int live_blocks = (rows_valid + 31) >> 5;
+  int ml_raw = (live_blocks - wm + WM - 1) / WM;
+  ml_raw = ml_raw < 0 ? 0 : (ml_raw > MB ? MB : ml_raw);
+  const int ml = __builtin_amdgcn_readfirstlane(ml_raw);
+  bool n_live[NB];
 #pragma unroll
   for (int j = 0; j < NB; ++j) n_live[j] = n0 + wn * WTN + j * 32 < N;
 
@@ -263,82 +278,138 @@ __global__ __launch_bounds__(WM* WN * 64) void grouped_gemm_kernel(GemmArgs g) {
   const int lrow = lane & 31;
   const int lk = lane >> 5;  // which K half of a sub-step this lane supplies
 
-  // a wave whose 64-row band holds no live row skips its MFMAs (the branch
-  // is wave-uniform; its LDS reads stay inside it)
-  const bool wave_live = __builtin_amdgcn_readfirstlane(wm * WTM < rows_valid ? 1 : 0) != 0;
-
-  auto compute = [&](int buf) {
-    if (!wave_live) return;
-    const uint8_t* A = As + buf * BM * kLds;
-    const uint8_t* B = Bs + buf * BN * kLds;
-    if constexpr (FMT == kFP8) {
+  // multiply the first ML row blocks of the wave out of LDS buffer buf
+  auto compute = [&](int buf, auto ml_c) {
+    constexpr int ML = decltype(ml_c)::value;
+    if constexpr (ML > 0) {
+      const uint8_t* A = As + buf * BM * kLds;
+      const uint8_t* B = Bs + buf * BN * kLds;
+      if constexpr (FMT == kFP8) {
 #pragma unroll
-      for (int s = 0; s < 2; ++s) {  // 64 K per MFMA
-        i32x8 af[MB], bfr[NB];
+        for (int s = 0; s < 2; ++s) {  // 64 K per MFMA
+          i32x8 af[ML], bfr[NB];
 #pragma unroll
-        for (int i = 0; i < MB; ++i) {
-          const uint8_t* p = A + (wm * WTM + i * 32 + lrow) * kLds + s * 64 + lk * 32;
-          const u32x4 lo = *reinterpret_cast<const u32x4*>(p);
-          const u32x4 hi = *reinterpret_cast<const u32x4*>(p + 16);
-          af[i] = i32x8{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3],
-                        (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
-        }
+          for (int i = 0; i < ML; ++i) {
+            const uint8_t* p = A + ((i * WM + wm) * 32 + lrow) * kLds + s * 64 + lk * 32;
+            const u32x4 lo = *reinterpret_cast<const u32x4*>(p);
+            const u32x4 hi = *reinterpret_cast<const u32x4*>(p + 16);
+            af[i] = i32x8{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3],
+                          (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
+          }
 #pragma unroll
-        for (int j = 0; j < NB; ++j) {
-          const uint8_t* p = B + (wn * WTN + j * 32 + lrow) * kLds + s * 64 + lk * 32;
-          const u32x4 lo = *reinterpret_cast<const u32x4*>(p);
-          const u32x4 hi = *reinterpret_cast<const u32x4*>(p + 16);
-          bfr[j] = i32x8{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3],
-                         (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
-        }
+          for (int j = 0; j < NB; ++j) {
+            const uint8_t* p = B + (wn * WTN + j * 32 + lrow) * kLds + s * 64 + lk * 32;
+            const u32x4 lo = *reinterpret_cast<const u32x4*>(p);
+            const u32x4 hi = *reinterpret_cast<const u32x4*>(p + 16);
+            bfr[j] = i32x8{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3],
+                           (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
+          }
 #pragma unroll
-        for (int i = 0; i < MB; ++i)
+          for (int i = 0; i < ML; ++i)
 #pragma unroll
-          for (int j = 0; j < NB; ++j)
-            acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+            for (int j = 0; j < NB; ++j)
+              acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
                   af[i], bfr[j], acc[i][j], 0, 0, 0, 127, 0, 127);
-      }
-    } else {
+        }
+      } else {
+        using frag = std::conditional_t<FMT == kNVFP4, f16x8, bf16x8>;
+        // fragments of sub-step s+1 are read while the MFMAs of sub-step s run
+        frag af[2][ML], bfr[2][NB];
+        auto rd = [&](int s, int slot) {
 #pragma unroll
-      for (int s = 0; s < 4; ++s) {  // 16 K per MFMA
-        bf16x8 af[MB], bfr[NB];
-#pragma unroll
-        for (int i = 0; i < MB; ++i)
-          af[i] = *reinterpret_cast<const bf16x8*>(
-              A + (wm * WTM + i * 32 + lrow) * kLds + s * 32 + lk * 16);
-#pragma unroll
-        for (int j = 0; j < NB; ++j)
-          bfr[j] = *reinterpret_cast<const bf16x8*>(
-              B + (wn * WTN + j * 32 + lrow) * kLds + s * 32 + lk * 16);
-#pragma unroll
-        for (int i = 0; i < MB; ++i)
+          for (int i = 0; i < ML; ++i)
+            af[slot][i] = *reinterpret_cast<const frag*>(
+                A + ((i * WM + wm) * 32 + lrow) * kLds + s * 32 + lk * 16);
 #pragma unroll
           for (int j = 0; j < NB; ++j)
-            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
+            bfr[slot][j] = *reinterpret_cast<const frag*>(
+                B + (wn * WTN + j * 32 + lrow) * kLds + s * 32 + lk * 16);
+        };
+        rd(0, 0);
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {  // 16 K per MFMA
+          if (s < 3) rd(s + 1, (s + 1) & 1);
+#pragma unroll
+          for (int i = 0; i < ML; ++i)
+#pragma unroll
+            for (int j = 0; j < NB; ++j) {
+              if constexpr (FMT == kNVFP4)
+                acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af[s & 1][i], bfr[s & 1][j],
+                                                                   acc[i][j], 0, 0, 0);
+              else
+                acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[s & 1][i], bfr[s & 1][j],
+                                                                    acc[i][j], 0, 0, 0);
+            }
+        }
+#if MOE_SCHED
+        // issue order: the first sub-step's reads, then each sub-step's MFMAs
+        // interleaved one for one with the next sub-step's reads
+        constexpr int RD = ML + NB, MF = ML * NB;
+        __builtin_amdgcn_sched_group_barrier(0x100, RD, 0);
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+#pragma unroll
+          for (int q = 0; q < MF; ++q) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            if (s < 3 && q < RD) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+          }
+          if (s < 3 && RD > MF) __builtin_amdgcn_sched_group_barrier(0x100, RD - MF, 0);
+        }
+#endif
       }
     }
   };
 
-  // ---- main loop: one barrier per K step (double-buffered LDS, loads two
-  // steps ahead).  Unrolled by two so register sets are compile-time indices;
-  // an odd step count runs one extra iteration that stores but does not compute.
+  // ---- main loop: one barrier per K step, double-buffered LDS, loads
+  // kPrefetch steps ahead in as many register sets.  Unrolled by kPrefetch so
+  // register sets are compile-time indices; trailing iterations past the last
+  // step store and load (clamped) but do not compute.
   using S0 = std::integral_constant<int, 0>;
   using S1 = std::integral_constant<int, 1>;
-  load(0, S0{});
-  load(1, S1{});
-  store(0, S0{});
-  load(2, S0{});
-  __syncthreads();
-  auto iter = [&](int step, auto set_next) {
-    // data of step+1 sits in register set (step+1)&1 == set_next
-    if (step < n_steps) compute(step & 1);
-    store((step + 1) & 1, set_next);
-    load(step + 3, set_next);
-    __syncthreads();
+  using S2 = std::integral_constant<int, 2>;
+  auto main_loop = [&](auto ml_c) {
+    auto iter = [&](int step, auto set_next) {
+      // data of step+1 sits in register set (step+1) % kPrefetch == set_next
+      if (step < n_steps) compute(step & 1, ml_c);
+      store((step + 1) & 1, set_next);
+      load(step + 1 + kPrefetch, set_next);
+      __syncthreads();
+    };
+    if constexpr (kPrefetch == 2) {
+      load(0, S0{});
+      load(1, S1{});
+      store(0, S0{});
+      load(2, S0{});
+      __syncthreads();
+      for (int step = 0; step < n_steps; step += 2) {
+        iter(step, S1{});
+        iter(step + 1, S0{});
+      }
+    } else {
+      load(0, S0{});
+      load(1, S1{});
+      load(2, S2{});
+      store(0, S0{});
+      load(3, S0{});
+      __syncthreads();
+      for (int step = 0; step < n_steps; step += 3) {
+        iter(step, S1{});
+        iter(step + 1, S2{});
+        iter(step + 2, S0{});
+      }
+    }
   };
-  for (int step = 0; step < n_steps; step += 2) {
-    iter(step, S1{});
-    iter(step + 1, S0{});
+  static_assert(MB <= 8, "row blocks per wave");
+  switch (ml) {
+    case 0: main_loop(std::integral_constant<int, 0>{}); break;
+    case 1: main_loop(std::integral_constant<int, (MB >= 1 ? 1 : MB)>{}); break;
+    case 2: main_loop(std::integral_constant<int, (MB >= 2 ? 2 : MB)>{}); break;
+    case 3: main_loop(std::integral_constant<int, (MB >= 3 ? 3 : MB)>{}); break;
+    case 4: main_loop(std::integral_constant<int, (MB >= 4 ? 4 : MB)>{}); break;
+    case 5: main_loop(std::integral_constant<int, (MB >= 5 ? 5 : MB)>{}); break;
+    case 6: main_loop(std::integral_constant<int, (MB >= 6 ? 6 : MB)>{}); break;
+    case 7: main_loop(std::integral_constant<int, (MB >= 7 ? 7 : MB)>{}); break;
+    default: main_loop(std::integral_constant<int, MB>{}); break;
   }
 
   // ---- epilogue.  32x32 f32 result: lane holds column lane%32 and rows
@@ -349,14 +420,14 @@ __global__ __launch_bounds__(WM* WN * 64) void grouped_gemm_kernel(GemmArgs g) {
   float local_max = 0.f;
 #pragma unroll
   for (int i = 0; i < MB; ++i) {
-    if (!m_live[i]) continue;
+    if (i >= ml) continue;
 #pragma unroll
     for (int j = 0; j < NB; ++j) {
       if (!n_live[j]) continue;
       const int col = n0 + wn * WTN + j * 32 + lrow;
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const int rl = wm * WTM + i * 32 + (r >> 2) * 8 + lk * 4 + (r & 3);
+        const int rl = (i * WM + wm) * 32 + (r >> 2) * 8 + lk * 4 + (r & 3);
         if (rl < rows_valid && col < N) {
           const size_t at = static_cast<size_t>(row0 + rl) * N + col;
           if constexpr (STAGE == 0) {
@@ -381,6 +452,306 @@ __global__ __launch_bounds__(WM* WN * 64) void grouped_gemm_kernel(GemmArgs g) {
     }
   }
   if constexpr (STAGE == 0 && FMT != kBF16) block_amax_to_slots(local_max, g.amax);
+}
+
+// ---------------------------------------------------------------------------
+// Prefill kernel with direct global -> LDS loads (global_load_lds_dwordx4) for
+// formats whose operands are staged as stored (BF16 both projections, FP8
+// down projection).  Per-thread ds_write staging costs about as much LDS time
+// as all the fragment reads of a step on this part; the direct loads move
+// each 16-byte chunk from L1 into LDS without passing through VGPRs.
+//
+// LDS holds NBUF buffers of [BM + BN] rows x 128 bytes (one K step), with no
+// padding: the 16-byte chunk c of row r sits in slot c ^ ((r >> 1) & 7), so
+// the 16 rows a quarter-wave ds_read_b128 touches at one chunk land on 16
+// distinct 4-bank groups.  A direct load writes one wave's 64 x 16 bytes to
+// consecutive LDS addresses (8 rows); each lane fetches the global chunk that
+// belongs in its slot.  Loads run NBUF - 1 steps ahead; at the top of each
+// step a wave waits for its own loads of that step (vmcnt) and the workgroup
+// meets at a barrier, after which every wave's loads are visible.
+
+__device__ __forceinline__ int lds_swz(int r) { return (r >> 1) & 7; }
+
+// s_waitcnt immediate that waits until at most n vector memory operations of
+// this wave are outstanding (expcnt and lgkmcnt left at their maxima)
+constexpr int vmcnt_imm(int n) { return (n & 15) | (7 << 4) | (15 << 8) | ((n >> 4) << 14); }
+
+template <int FMT, int STAGE, int BM, int BN, int WM, int WN, int NBUF>
+__global__ __launch_bounds__(WM* WN * 64) void grouped_gemm_dma_kernel(GemmArgs g) {
+  static_assert(FMT == kBF16 || FMT == kFP8, "operands staged as stored");
+  static_assert(NBUF >= 2 && NBUF <= 4, "buffers");
+  constexpr int NW = WM * WN;
+  constexpr int WTM = BM / WM, WTN = BN / WN;
+  constexpr int MB = WTM / 32, NB = WTN / 32;
+  constexpr int ESZ = (FMT == kFP8) ? 1 : 2;
+  constexpr int QA = BM / 8 / NW, QB = BN / 8 / NW;  // direct loads per wave per step
+  static_assert(QA * NW * 8 == BM && QB * NW * 8 == BN, "tile rows per wave");
+  static_assert(BM % 16 == 0, "swizzle period");
+  constexpr int DPS = QA + QB;  // vector memory operations per wave per step
+  constexpr int BUF = (BM + BN) * 128;
+  __shared__ __attribute__((aligned(1024))) uint8_t lds0[BUF];
+  __shared__ __attribute__((aligned(1024))) uint8_t lds1[BUF];
+  __shared__ __attribute__((aligned(1024))) uint8_t lds2[NBUF >= 3 ? BUF : 1024];
+  __shared__ __attribute__((aligned(1024))) uint8_t lds3[NBUF >= 4 ? BUF : 1024];
+
+  // ---- which tile (same order as grouped_gemm_kernel)
+  const int n_ntiles = (g.N + BN - 1) / BN;
+  const int total = g.tile_off[g.E] * n_ntiles;
+  const int per_xcd = (total + 7) >> 3;
+  const int local = blockIdx.x >> 3;
+  if (local >= per_xcd) return;
+  const int logical = (blockIdx.x & 7) * per_xcd + local;
+  if (logical >= total) return;
+  int lo = 0, hi = g.E;
+  while (hi - lo > 1) {
+    const int mid = (lo + hi) >> 1;
+    if (g.tile_off[mid] * n_ntiles <= logical) lo = mid; else hi = mid;
+  }
+  const int e = lo;
+  const int te = g.tile_off[e + 1] - g.tile_off[e];
+  const int loc = logical - g.tile_off[e] * n_ntiles;
+  const int ntile = loc / te;
+  const int mt = loc - ntile * te;
+  const int row0 = g.offsets[e] + mt * BM;
+  const int rows_valid = min(BM, g.offsets[e + 1] - row0);
+  const int n0 = ntile * BN;
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave / WN, wn = wave % WN;
+  const int K = g.K, N = g.N;
+  const int k_bytes = K * ESZ;
+  const int n_steps = (k_bytes + 127) / 128;
+
+  // ---- per-lane global sources of the direct loads (fixed over K)
+  const uint8_t* a_src[QA];
+  int a_cof[QA];
+#pragma unroll
+  for (int q = 0; q < QA; ++q) {
+    const int r = (wave + q * NW) * 8 + (lane >> 3);
+    const int c = (lane & 7) ^ lds_swz(r);
+    const int rr = min(r, rows_valid - 1);
+    size_t src;
+    if constexpr (STAGE == 0) {
+      src = static_cast<size_t>(g.sorted_src[row0 + rr] / g.top_k);
+    } else {
+      src = static_cast<size_t>(row0 + rr);
+    }
+    a_src[q] = static_cast<const uint8_t*>(g.a) + src * k_bytes + c * 16;
+    a_cof[q] = c * 16;
+  }
+  const uint8_t* b_src[QB];
+  int b_cof[QB];
+#pragma unroll
+  for (int q = 0; q < QB; ++q) {
+    const int r = (wave + q * NW) * 8 + (lane >> 3);
+    const int c = (lane & 7) ^ lds_swz(r);
+    const int n = min(n0 + r, N - 1);
+    b_src[q] = static_cast<const uint8_t*>(g.b) + (static_cast<size_t>(e) * N + n) * k_bytes + c * 16;
+    b_cof[q] = c * 16;
+  }
+
+  // issue the direct loads of one K step into buffer buf.  Steps past the end
+  // re-read the last step (the buffer is not read again); a chunk past the
+  // FP8 K tail reads the in-range chunk 64 bytes earlier and is zeroed when
+  // the fragments are formed.
+  auto dma = [&](int step_in, uint8_t* buf) {
+    const int step = min(step_in, n_steps - 1);
+    const int kb = step * 128;
+#pragma unroll
+    for (int q = 0; q < QA; ++q) {
+      const uint8_t* p = a_src[q] + kb;
+      if constexpr (FMT == kFP8) p = (kb + a_cof[q] >= k_bytes) ? p - 64 : p;
+      __builtin_amdgcn_global_load_lds(
+          p, (__attribute__((address_space(3))) void*)(buf + (wave + q * NW) * 1024), 16, 0, 0);
+    }
+#pragma unroll
+    for (int q = 0; q < QB; ++q) {
+      const uint8_t* p = b_src[q] + kb;
+      if constexpr (FMT == kFP8) p = (kb + b_cof[q] >= k_bytes) ? p - 64 : p;
+      __builtin_amdgcn_global_load_lds(
+          p, (__attribute__((address_space(3))) void*)(buf + BM * 128 + (wave + q * NW) * 1024),
+          16, 0, 0);
+    }
+  };
+
+  // row blocks dealt to wave rows in turn (as in grouped_gemm_kernel)
+  const int live_blocks = (rows_valid + 31) >> 5;
+  int ml_raw = (live_blocks - wm + WM - 1) / WM;
+  ml_raw = ml_raw < 0 ? 0 : (ml_raw > MB ? MB : ml_raw);
+  const int ml = __builtin_amdgcn_readfirstlane(ml_raw);
+  bool n_live[NB];
+#pragma unroll
+  for (int j = 0; j < NB; ++j) n_live[j] = n0 + wn * WTN + j * 32 < N;
+
+  f32x16 acc[MB][NB];
+#pragma unroll
+  for (int i = 0; i < MB; ++i)
+#pragma unroll
+    for (int j = 0; j < NB; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+
+  const int lrow = lane & 31;
+  const int lk = lane >> 5;
+  // byte offsets of this lane's rows inside a buffer, and their swizzles
+  int a_row[MB], a_sw[MB], b_row[NB], b_sw[NB];
+#pragma unroll
+  for (int i = 0; i < MB; ++i) {
+    const int r = (i * WM + wm) * 32 + lrow;
+    a_row[i] = r * 128;
+    a_sw[i] = lds_swz(r);
+  }
+#pragma unroll
+  for (int j = 0; j < NB; ++j) {
+    const int r = wn * WTN + j * 32 + lrow;
+    b_row[j] = BM * 128 + r * 128;
+    b_sw[j] = lds_swz(r);
+  }
+
+  auto compute = [&](const uint8_t* buf, int step, auto ml_c) {
+    constexpr int ML = decltype(ml_c)::value;
+    if constexpr (ML > 0) {
+      if constexpr (FMT == kFP8) {
+        // the second 64-byte half of the last step lies past K when K % 128 == 64
+        const bool tail = (step * 128 + 64 >= k_bytes);
+#pragma unroll
+        for (int s = 0; s < 2; ++s) {  // 64 K per MFMA: chunks 4s + 2lk, +1
+          i32x8 af[ML], bfr[NB];
+          const int c0 = s * 4 + lk * 2;
+#pragma unroll
+          for (int i = 0; i < ML; ++i) {
+            const u32x4 x0 = *reinterpret_cast<const u32x4*>(buf + a_row[i] + ((c0 ^ a_sw[i]) << 4));
+            const u32x4 x1 = *reinterpret_cast<const u32x4*>(buf + a_row[i] + (((c0 + 1) ^ a_sw[i]) << 4));
+            af[i] = i32x8{(int)x0[0], (int)x0[1], (int)x0[2], (int)x0[3],
+                          (int)x1[0], (int)x1[1], (int)x1[2], (int)x1[3]};
+          }
+#pragma unroll
+          for (int j = 0; j < NB; ++j) {
+            const u32x4 x0 = *reinterpret_cast<const u32x4*>(buf + b_row[j] + ((c0 ^ b_sw[j]) << 4));
+            const u32x4 x1 = *reinterpret_cast<const u32x4*>(buf + b_row[j] + (((c0 + 1) ^ b_sw[j]) << 4));
+            bfr[j] = i32x8{(int)x0[0], (int)x0[1], (int)x0[2], (int)x0[3],
+                           (int)x1[0], (int)x1[1], (int)x1[2], (int)x1[3]};
+            if (s == 1 && tail) bfr[j] = i32x8{0, 0, 0, 0, 0, 0, 0, 0};
+          }
+          if (s == 1 && tail) {
+#pragma unroll
+            for (int i = 0; i < ML; ++i) af[i] = i32x8{0, 0, 0, 0, 0, 0, 0, 0};
+          }
+#pragma unroll
+          for (int i = 0; i < ML; ++i)
+#pragma unroll
+            for (int j = 0; j < NB; ++j)
+              acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+                  af[i], bfr[j], acc[i][j], 0, 0, 0, 127, 0, 127);
+        }
+      } else {
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {  // 16 K per MFMA: chunk 2s + lk
+          const int c = s * 2 + lk;
+          bf16x8 af[ML], bfr[NB];
+#pragma unroll
+          for (int i = 0; i < ML; ++i)
+            af[i] = *reinterpret_cast<const bf16x8*>(buf + a_row[i] + ((c ^ a_sw[i]) << 4));
+#pragma unroll
+          for (int j = 0; j < NB; ++j)
+            bfr[j] = *reinterpret_cast<const bf16x8*>(buf + b_row[j] + ((c ^ b_sw[j]) << 4));
+#pragma unroll
+          for (int i = 0; i < ML; ++i)
+#pragma unroll
+            for (int j = 0; j < NB; ++j)
+              acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
+        }
+      }
+    }
+  };
+
+  // one K step: wait for this wave's loads of the step, meet, start the loads
+  // NBUF - 1 steps ahead into the buffer everyone finished reading, multiply
+  auto body = [&](int step, const uint8_t* cur, uint8_t* ahead, auto ml_c) {
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm((NBUF - 2) * DPS));
+    __asm__ volatile("s_barrier" ::: "memory");
+    dma(step + NBUF - 1, ahead);
+    if (step < n_steps) compute(cur, step, ml_c);
+  };
+  auto main_loop = [&](auto ml_c) {
+    dma(0, lds0);
+    if constexpr (NBUF == 4) {
+      dma(1, lds1);
+      dma(2, lds2);
+      for (int step = 0; step < n_steps; step += 4) {
+        body(step, lds0, lds3, ml_c);
+        body(step + 1, lds1, lds0, ml_c);
+        body(step + 2, lds2, lds1, ml_c);
+        body(step + 3, lds3, lds2, ml_c);
+      }
+    } else if constexpr (NBUF == 3) {
+      dma(1, lds1);
+      for (int step = 0; step < n_steps; step += 3) {
+        body(step, lds0, lds2, ml_c);
+        body(step + 1, lds1, lds0, ml_c);
+        body(step + 2, lds2, lds1, ml_c);
+      }
+    } else {
+      for (int step = 0; step < n_steps; step += 2) {
+        body(step, lds0, lds1, ml_c);
+        body(step + 1, lds1, lds0, ml_c);
+      }
+    }
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+  };
+  static_assert(MB <= 4, "row blocks per wave");
+  switch (ml) {
+    case 0: main_loop(std::integral_constant<int, 0>{}); break;
+    case 1: main_loop(std::integral_constant<int, (MB >= 1 ? 1 : MB)>{}); break;
+    case 2: main_loop(std::integral_constant<int, (MB >= 2 ? 2 : MB)>{}); break;
+    case 3: main_loop(std::integral_constant<int, (MB >= 3 ? 3 : MB)>{}); break;
+    default: main_loop(std::integral_constant<int, MB>{}); break;
+  }
+
+  // ---- epilogue (as in grouped_gemm_kernel)
+  double scale = 1.0;
+  if constexpr (FMT != kBF16) scale = static_cast<double>(g.a_s[0]) * static_cast<double>(g.b_s[e]);
+#pragma unroll
+  for (int i = 0; i < MB; ++i) {
+    if (i >= ml) continue;
+#pragma unroll
+    for (int j = 0; j < NB; ++j) {
+      if (!n_live[j]) continue;
+      const int col = n0 + wn * WTN + j * 32 + lrow;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int rl = (i * WM + wm) * 32 + (r >> 2) * 8 + lk * 4 + (r & 3);
+        if (rl < rows_valid && col < N) {
+          const size_t at = static_cast<size_t>(row0 + rl) * N + col;
+          if constexpr (STAGE == 0) {
+            static_assert(FMT == kBF16, "the FP8 up projection runs in grouped_gemm_kernel");
+            const double h = static_cast<double>(acc[i][j][r]);
+            static_cast<uint16_t*>(g.out)[at] = h > 0.0 ? f64_to_bf16(h * h) : static_cast<uint16_t>(0);
+          } else {
+            const float gate = g.row_gate[row0 + rl];
+            float o;
+            if constexpr (FMT == kBF16) {
+              o = acc[i][j][r] * gate;
+            } else {
+              o = static_cast<float>(static_cast<double>(acc[i][j][r]) * scale * gate);
+            }
+            static_cast<float*>(g.out)[at] = o;
+          }
+        }
+      }
+    }
+  }
+}
+
+template <int FMT, int STAGE, int BM, int BN, int WM, int WN, int NBUF>
+hipError_t launch_dma(const GemmArgs& g, hipStream_t stream) {
+  const int n_ntiles = (g.N + BN - 1) / BN;
+  long long blocks = static_cast<long long>(g.max_tiles) * n_ntiles;
+  blocks = (blocks + 7) / 8 * 8;
+  if (blocks <= 0) return hipSuccess;
+  hipLaunchKernelGGL((grouped_gemm_dma_kernel<FMT, STAGE, BM, BN, WM, WN, NBUF>), dim3(blocks),
+                     dim3(WM * WN * 64), 0, stream, g);
+  return hipGetLastError();
 }
 
 template <int FMT, int STAGE, int BM, int BN, int WM, int WN>
@@ -425,21 +796,82 @@ constexpr int kPBM = 256, kPBN = 256, kPWM = 4, kPWN = 2;
 constexpr int kPBM = 256, kPBN = 128, kPWM = 4, kPWN = 2;
 #elif MOE_PREFILL_CFG == 12
 constexpr int kPBM = 128, kPBN = 256, kPWM = 2, kPWN = 2;
+#elif MOE_PREFILL_CFG == 13
+constexpr int kPBM = 128, kPBN = 256, kPWM = 1, kPWN = 4;
+#elif MOE_PREFILL_CFG == 14
+constexpr int kPBM = 256, kPBN = 256, kPWM = 2, kPWN = 4;
+#elif MOE_PREFILL_CFG == 15
+constexpr int kPBM = 256, kPBN = 128, kPWM = 2, kPWN = 4;
+#elif MOE_PREFILL_CFG == 16
+constexpr int kPBM = 128, kPBN = 128, kPWM = 1, kPWN = 4;
+#elif MOE_PREFILL_CFG == 17
+constexpr int kPBM = 256, kPBN = 128, kPWM = 2, kPWN = 2;
+#elif MOE_PREFILL_CFG == 18
+constexpr int kPBM = 256, kPBN = 256, kPWM = 2, kPWN = 2;
+#elif MOE_PREFILL_CFG == 19
+constexpr int kPBM = 128, kPBN = 128, kPWM = 2, kPWN = 2;
+#elif MOE_PREFILL_CFG == 20
+constexpr int kPBM = 256, kPBN = 128, kPWM = 4, kPWN = 1;
 #else
 #error "unknown MOE_PREFILL_CFG"
 #endif
 
+// Direct-load prefill shape (MOE_DMA_CFG selects alternatives for comparison)
+#ifndef MOE_DMA_CFG
+#define MOE_DMA_CFG 0
+#endif
+#if MOE_DMA_CFG == 0
+constexpr int kDBM = 128, kDBN = 128, kDWM = 2, kDWN = 4, kDBUF = 2;
+#elif MOE_DMA_CFG == 1
+constexpr int kDBM = 128, kDBN = 128, kDWM = 2, kDWN = 4, kDBUF = 3;
+#elif MOE_DMA_CFG == 2
+constexpr int kDBM = 128, kDBN = 128, kDWM = 2, kDWN = 2, kDBUF = 2;
+#elif MOE_DMA_CFG == 3
+constexpr int kDBM = 128, kDBN = 128, kDWM = 2, kDWN = 2, kDBUF = 3;
+#elif MOE_DMA_CFG == 4
+constexpr int kDBM = 128, kDBN = 256, kDWM = 2, kDWN = 4, kDBUF = 2;
+#elif MOE_DMA_CFG == 5
+constexpr int kDBM = 256, kDBN = 128, kDWM = 4, kDWN = 2, kDBUF = 2;
+#elif MOE_DMA_CFG == 6
+constexpr int kDBM = 128, kDBN = 256, kDWM = 2, kDWN = 4, kDBUF = 3;
+#elif MOE_DMA_CFG == 7
+constexpr int kDBM = 128, kDBN = 128, kDWM = 2, kDWN = 4, kDBUF = 4;
+#elif MOE_DMA_CFG == 8
+constexpr int kDBM = 64, kDBN = 128, kDWM = 2, kDWN = 4, kDBUF = 3;
+#elif MOE_DMA_CFG == 9
+constexpr int kDBM = 128, kDBN = 64, kDWM = 4, kDWN = 2, kDBUF = 3;
+#elif MOE_DMA_CFG == 10
+constexpr int kDBM = 64, kDBN = 128, kDWM = 1, kDWN = 4, kDBUF = 4;
+#elif MOE_DMA_CFG == 11
+constexpr int kDBM = 128, kDBN = 128, kDWM = 2, kDWN = 2, kDBUF = 4;
+#else
+#error "unknown MOE_DMA_CFG"
+#endif
+
+// prefill projections whose operands are staged as stored use the direct-load kernel
+constexpr bool uses_dma(int fmt, int stage) {
+  return fmt == kBF16 || (fmt == kFP8 && stage == 1);
+}
+
 template <int FMT, int STAGE>
 hipError_t launch_fmt_stage(int T, const GemmArgs& g, hipStream_t stream) {
-  const GemmShape s = gemm_shape(FMT, STAGE, T);
+  const GemmShape s = gemm_shape(FMT == kFP8X ? kFP8 : FMT, STAGE, T);
   if (s.bm == 32) return launch_one<FMT, STAGE, 32, 128, 1, 4>(g, stream);
+  if constexpr (FMT == kBF16 || (FMT == kFP8 && STAGE == 1))
+    return launch_dma<FMT, STAGE, kDBM, kDBN, kDWM, kDWN, kDBUF>(g, stream);
+#if MOE_PREFILL_CFG == 2
+  // NVFP4 expands its weight codes in registers: 64x64 wave tiles (four waves)
+  // measured faster than 64x32 ones for both projections
+  if constexpr (FMT == kNVFP4) return launch_one<FMT, STAGE, 128, 128, 2, 2>(g, stream);
+#endif
   return launch_one<FMT, STAGE, kPBM, kPBN, kPWM, kPWN>(g, stream);
 }
 
 }  // namespace
 
-GemmShape gemm_shape(int /*fmt*/, int /*stage*/, int T) {
+GemmShape gemm_shape(int fmt, int stage, int T) {
   if (T < 512) return GemmShape{32, 128};
+  if (uses_dma(fmt, stage)) return GemmShape{kDBM, kDBN};
   return GemmShape{kPBM, kPBN};
 }
 

@@ -12,7 +12,8 @@
 // per-chunk expert counts; perm_scan (one workgroup) turns them into chunk
 // bases, expert offsets and per-expert row-tile prefixes for the GEMMs;
 // perm_scatter recomputes each entry's stable rank inside its chunk with wave
-// ballots.  No host sync.
+// ballots.  When all ids fit one chunk (decode batches) perm_single does the
+// three steps in one workgroup.  No host sync.
 #include "moe_common.h"
 #include "moe_internal.h"
 
@@ -23,12 +24,10 @@ namespace {
 constexpr int kPermThreads = 256;
 constexpr int kRounds = kChunk / kPermThreads;  // entries per thread per chunk
 
-__global__ __launch_bounds__(kPermThreads) void perm_count_kernel(
-    const int32_t* __restrict__ ids, int R, int E, int32_t* __restrict__ chunk_counts) {
-  __shared__ int32_t cnt[256];
-  for (int e = threadIdx.x; e < E; e += kPermThreads) cnt[e] = 0;
-  __syncthreads();
-  const int base = blockIdx.x * kChunk;
+// per-expert counts of one chunk of flat ids into LDS cnt[] (zeroed by the caller)
+__device__ void count_chunk(const int32_t* __restrict__ ids, int R, int E, int chunk,
+                            int32_t* cnt) {
+  const int base = chunk * kChunk;
   for (int r = 0; r < kRounds; ++r) {
     const int i = base + r * kPermThreads + threadIdx.x;
     if (i < R) {
@@ -36,6 +35,14 @@ __global__ __launch_bounds__(kPermThreads) void perm_count_kernel(
       if (e >= 0 && e < E) atomicAdd(&cnt[e], 1);
     }
   }
+}
+
+__global__ __launch_bounds__(kPermThreads) void perm_count_kernel(
+    const int32_t* __restrict__ ids, int R, int E, int32_t* __restrict__ chunk_counts) {
+  __shared__ int32_t cnt[256];
+  for (int e = threadIdx.x; e < E; e += kPermThreads) cnt[e] = 0;
+  __syncthreads();
+  count_chunk(ids, R, E, blockIdx.x, cnt);
   __syncthreads();
   for (int e = threadIdx.x; e < E; e += kPermThreads)
     chunk_counts[static_cast<size_t>(blockIdx.x) * E + e] = cnt[e];
@@ -62,23 +69,16 @@ __device__ int block_exclusive_scan(int v, int* tmp, int& total) {
   return wbase + incl - v;
 }
 
-__global__ __launch_bounds__(kPermThreads) void perm_scan_kernel(
-    const int32_t* __restrict__ chunk_counts, int n_chunks, int E,
-    int32_t* __restrict__ chunk_base, int32_t* __restrict__ counts,
-    int32_t* __restrict__ offsets, int bm0, int32_t* __restrict__ tile_off0, int bm1,
-    int32_t* __restrict__ tile_off1, uint32_t* __restrict__ zero_words, int n_zero) {
-  __shared__ int tmp[kPermThreads / 64];
+// expert offsets and both GEMM tile prefixes from the total count `run` of
+// expert e = threadIdx.x (0 when e >= E); zeroes the words the later stages
+// accumulate into
+__device__ void scan_experts(int run, int E, int32_t* __restrict__ counts,
+                             int32_t* __restrict__ offsets, int bm0, int32_t* __restrict__ tile_off0,
+                             int bm1, int32_t* __restrict__ tile_off1,
+                             uint32_t* __restrict__ zero_words, int n_zero, int* tmp) {
   const int e = threadIdx.x;
   for (int i = threadIdx.x; i < n_zero; i += kPermThreads) zero_words[i] = 0u;
-  int run = 0;
-  if (e < E) {
-    for (int c = 0; c < n_chunks; ++c) {
-      const size_t at = static_cast<size_t>(c) * E + e;
-      chunk_base[at] = run;
-      run += chunk_counts[at];
-    }
-    counts[e] = run;
-  }
+  if (e < E) counts[e] = run;
   int total;
   const int off = block_exclusive_scan(e < E ? run : 0, tmp, total);
   if (e < E) offsets[e] = off;
@@ -96,21 +96,32 @@ __global__ __launch_bounds__(kPermThreads) void perm_scan_kernel(
   }
 }
 
-__global__ __launch_bounds__(kPermThreads) void perm_scatter_kernel(
-    const int32_t* __restrict__ ids, const float* __restrict__ gates, int R, int E, int k,
-    const int32_t* __restrict__ chunk_base, const int32_t* __restrict__ offsets,
-    int32_t* __restrict__ sorted_src, int32_t* __restrict__ inv,
-    float* __restrict__ row_gate) {
-  __shared__ int32_t run[256];
-  __shared__ int32_t wcnt[kPermThreads / 64][256];
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  for (int e = threadIdx.x; e < E; e += kPermThreads) {
-    run[e] = offsets[e] + chunk_base[static_cast<size_t>(blockIdx.x) * E + e];
+__global__ __launch_bounds__(kPermThreads) void perm_scan_kernel(
+    const int32_t* __restrict__ chunk_counts, int n_chunks, int E,
+    int32_t* __restrict__ chunk_base, int32_t* __restrict__ counts,
+    int32_t* __restrict__ offsets, int bm0, int32_t* __restrict__ tile_off0, int bm1,
+    int32_t* __restrict__ tile_off1, uint32_t* __restrict__ zero_words, int n_zero) {
+  __shared__ int tmp[kPermThreads / 64];
+  const int e = threadIdx.x;
+  int run = 0;
+  if (e < E) {
+    for (int c = 0; c < n_chunks; ++c) {
+      const size_t at = static_cast<size_t>(c) * E + e;
+      chunk_base[at] = run;
+      run += chunk_counts[at];
+    }
   }
-  for (int i = threadIdx.x; i < (kPermThreads / 64) * 256; i += kPermThreads)
-    (&wcnt[0][0])[i] = 0;
-  __syncthreads();
-  const int base = blockIdx.x * kChunk;
+  scan_experts(run, E, counts, offsets, bm0, tile_off0, bm1, tile_off1, zero_words, n_zero, tmp);
+}
+
+// stable scatter of one chunk; run[e] (LDS) holds the first sorted row of
+// expert e for this chunk and advances past it
+__device__ void scatter_chunk(const int32_t* __restrict__ ids, const float* __restrict__ gates,
+                              int R, int E, int chunk, int32_t* run, int32_t (*wcnt)[256],
+                              int32_t* __restrict__ sorted_src, int32_t* __restrict__ inv,
+                              float* __restrict__ row_gate) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int base = chunk * kChunk;
   const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
   for (int r = 0; r < kRounds; ++r) {
     const int i = base + r * kPermThreads + threadIdx.x;
@@ -152,12 +163,61 @@ __global__ __launch_bounds__(kPermThreads) void perm_scatter_kernel(
   }
 }
 
+__global__ __launch_bounds__(kPermThreads) void perm_scatter_kernel(
+    const int32_t* __restrict__ ids, const float* __restrict__ gates, int R, int E, int k,
+    const int32_t* __restrict__ chunk_base, const int32_t* __restrict__ offsets,
+    int32_t* __restrict__ sorted_src, int32_t* __restrict__ inv,
+    float* __restrict__ row_gate) {
+  __shared__ int32_t run[256];
+  __shared__ int32_t wcnt[kPermThreads / 64][256];
+  for (int e = threadIdx.x; e < E; e += kPermThreads) {
+    run[e] = offsets[e] + chunk_base[static_cast<size_t>(blockIdx.x) * E + e];
+  }
+  for (int i = threadIdx.x; i < (kPermThreads / 64) * 256; i += kPermThreads)
+    (&wcnt[0][0])[i] = 0;
+  __syncthreads();
+  scatter_chunk(ids, gates, R, E, blockIdx.x, run, wcnt, sorted_src, inv, row_gate);
+}
+
+// All three steps in one workgroup when the flat ids fit one chunk (decode
+// batches): saves two launches on the latency-bound path.
+__global__ __launch_bounds__(kPermThreads) void perm_single_kernel(
+    const int32_t* __restrict__ ids, const float* __restrict__ gates, int R, int E,
+    int32_t* __restrict__ counts, int32_t* __restrict__ offsets, int bm0,
+    int32_t* __restrict__ tile_off0, int bm1, int32_t* __restrict__ tile_off1,
+    uint32_t* __restrict__ zero_words, int n_zero, int32_t* __restrict__ sorted_src,
+    int32_t* __restrict__ inv, float* __restrict__ row_gate) {
+  __shared__ int32_t cnt[256];
+  __shared__ int32_t wcnt[kPermThreads / 64][256];
+  __shared__ int tmp[kPermThreads / 64];
+  for (int e = threadIdx.x; e < 256; e += kPermThreads) cnt[e] = 0;
+  for (int i = threadIdx.x; i < (kPermThreads / 64) * 256; i += kPermThreads)
+    (&wcnt[0][0])[i] = 0;
+  __syncthreads();
+  count_chunk(ids, R, E, 0, cnt);
+  __syncthreads();
+  const int e = threadIdx.x;
+  const int run = e < E ? cnt[e] : 0;
+  scan_experts(run, E, counts, offsets, bm0, tile_off0, bm1, tile_off1, zero_words, n_zero, tmp);
+  __syncthreads();
+  // cnt[] becomes the running first row of each expert
+  if (e < E) cnt[e] = offsets[e];
+  __syncthreads();
+  scatter_chunk(ids, gates, R, E, 0, cnt, wcnt, sorted_src, inv, row_gate);
+}
+
 }  // namespace
 
 hipError_t launch_permute(const int32_t* ids, const float* gates, int T, int E, int k,
                           const PermBufs& p, hipStream_t stream) {
   const int R = T * k;
   const int n_chunks = (R + kChunk - 1) / kChunk;
+  if (n_chunks <= 1) {
+    hipLaunchKernelGGL(perm_single_kernel, dim3(1), dim3(kPermThreads), 0, stream, ids, gates, R,
+                       E, p.counts, p.offsets, p.bm0, p.tile_off0, p.bm1, p.tile_off1,
+                       p.zero_words, p.n_zero, p.sorted_src, p.inv, p.row_gate);
+    return hipGetLastError();
+  }
   hipLaunchKernelGGL(perm_count_kernel, dim3(n_chunks), dim3(kPermThreads), 0, stream, ids, R,
                      E, p.chunk_counts);
   hipLaunchKernelGGL(perm_scan_kernel, dim3(1), dim3(kPermThreads), 0, stream,

@@ -88,9 +88,10 @@ __global__ __launch_bounds__(kQThreads) void quant_fp8_kernel(const uint16_t* __
   }
 }
 
-// NVFP4: one 16-element block per thread.  mode 0 writes the bf16 values
-// dec(q) * dec(sb) (exact in bf16) into deq, which may alias x; mode 1 writes
-// packed codes and block scale codes.
+// NVFP4: one 16-element block per thread.  mode 0 writes the fp16 values
+// dec(q) * dec(sb) into deq, which may alias x (at most 6 significant bits and
+// inside [2^-10, 2688]: exact in fp16, the operand type of the NVFP4 GEMM);
+// mode 1 writes packed codes and block scale codes.
 __global__ __launch_bounds__(kQThreads) void quant_nvfp4_kernel(
     const uint16_t* x, const int32_t* n_rows_dev, int rows, int cols, const uint32_t* amax_p,
     int mode, uint16_t* deq, uint8_t* __restrict__ codes, uint8_t* __restrict__ bs,
@@ -135,9 +136,10 @@ __global__ __launch_bounds__(kQThreads) void quant_nvfp4_kernel(
       uint32_t o[8];
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
-        const float d0 = e2m1_decode(q[2 * j]) * sbf;  // exact
-        const float d1 = e2m1_decode(q[2 * j + 1]) * sbf;
-        o[j] = (__float_as_uint(d0) >> 16) | (__float_as_uint(d1) & 0xffff0000u);
+        const _Float16 d0 = static_cast<_Float16>(e2m1_decode(q[2 * j]) * sbf);  // exact
+        const _Float16 d1 = static_cast<_Float16>(e2m1_decode(q[2 * j + 1]) * sbf);
+        o[j] = static_cast<uint32_t>(__builtin_bit_cast(uint16_t, d0)) |
+               (static_cast<uint32_t>(__builtin_bit_cast(uint16_t, d1)) << 16);
       }
       reinterpret_cast<u32x4*>(deq)[2 * i] = u32x4{o[0], o[1], o[2], o[3]};
       reinterpret_cast<u32x4*>(deq)[2 * i + 1] = u32x4{o[4], o[5], o[6], o[7]};
