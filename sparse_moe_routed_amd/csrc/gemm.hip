@@ -6,26 +6,31 @@
 // multiplied together (grouped expert matmul, audio.cpp notes, section "CPU
 // weight offload").
 //
-// One kernel template serves both projections and all three weight formats.
 // A workgroup computes a BM x BN tile of one expert: BM sorted rows of that
 // expert (row tiles counted by the permutation on the device) times BN output
-// columns.
-// Both operands are K-contiguous; each K step moves 128 bytes of every A and
-// B row through double-buffered LDS (rows padded to 144 bytes, which keeps
-// the 16-byte MFMA operand reads of 16 consecutive rows on distinct banks).
+// columns.  Both operands are K-contiguous.  Two kernels, one per regime:
+//   grouped_gemm_kernel (decode batches, 32-row tiles): weight streaming; each
+//     thread loads 16-byte chunks two K steps ahead into registers and stores
+//     them into double-buffered LDS (rows padded to 144 bytes); weight codes
+//     of the expanded formats are converted on the way into LDS.
+//   grouped_gemm_dma_kernel (prefill, 128-row tiles): operands go from global
+//     memory straight into LDS (global_load_lds_dwordx4) as stored, into an
+//     XOR-swizzled layout; weight codes are expanded per lane when the MFMA
+//     fragments are formed.  See the comment above that kernel.
+// Formats:
 //   BF16 : v_mfma_f32_32x32x16_bf16, 64 K per step.
 //   FP8  : v_mfma_scale_f32_32x32x64_f8f6f4 with unit E8M0 scales (E4M3 x
 //          E4M3), 128 K per step; a 64-byte K tail (K = 1856 = 14*128 + 64)
-//          is zero-filled in LDS rather than padded in HBM (zero padding of K
+//          is zeroed on chip rather than padded in HBM (zero padding of K
 //          with matching zero activations leaves results unchanged: audio.cpp
 //          notes, section "Q4_K, Q3_K and Q2_K expert profiles").
-//   FP8X : E4M3 weight codes expanded to bf16 while staged into LDS
-//          (v_cvt_scalef32_pk_bf16_fp8 with unit scale, exact), then the BF16
-//          MFMA on bf16 activations holding dec(code).  Used for the FP8 up
-//          projection: the FP8 MFMA sums its 64 products with a short internal
-//          significand (about 13 bits below the largest product), and the up
-//          projection's output is re-quantised, so that error would move
-//          intermediate E4M3 codes; exact products with fp32 sums do not.
+//   FP8X : E4M3 weight codes expanded to bf16 (v_cvt_scalef32_pk_bf16_fp8 with
+//          unit scale, exact), then the BF16 MFMA on bf16 activations holding
+//          dec(code).  Used for the FP8 up projection: the FP8 MFMA sums its 64
+//          products with a short internal significand (about 13 bits below
+//          the largest product), and the up projection's output is
+//          re-quantised, so that error would move intermediate E4M3 codes;
+//          exact products with fp32 sums do not.
 //   NVFP4: E2M1 codes expanded to fp16 with v_cvt_scalef32_pk_f16_fp4 (unit
 //          scale) and multiplied by the E4M3 block scale with v_pk_mul_f16:
 //          code * block scale has at most 6 significant bits and lies in
@@ -45,14 +50,7 @@ namespace moe {
 namespace {
 
 constexpr int kStepBytes = 128;  // K bytes of each A/B row staged per step
-#ifndef MOE_PREFETCH
-#define MOE_PREFETCH 2
-#endif
-constexpr int kPrefetch = MOE_PREFETCH;  // K steps of loads in flight per thread
-static_assert(kPrefetch == 2 || kPrefetch == 3, "prefetch depth");
-#ifndef MOE_SCHED
-#define MOE_SCHED 1
-#endif
+constexpr int kPrefetch = 2;     // K steps of loads in flight per thread
 constexpr int kLds = 144;        // padded LDS row stride in bytes
 
 template <int FMT, int STAGE, int BM, int BN, int WM, int WN>
@@ -341,62 +339,32 @@ __global__ __launch_bounds__(WM* WN * 64) void grouped_gemm_kernel(GemmArgs g) {
                                                                     acc[i][j], 0, 0, 0);
             }
         }
-#if MOE_SCHED
-        // issue order: the first sub-step's reads, then each sub-step's MFMAs
-        // interleaved one for one with the next sub-step's reads
-        constexpr int RD = ML + NB, MF = ML * NB;
-        __builtin_amdgcn_sched_group_barrier(0x100, RD, 0);
-#pragma unroll
-        for (int s = 0; s < 4; ++s) {
-#pragma unroll
-          for (int q = 0; q < MF; ++q) {
-            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-            if (s < 3 && q < RD) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-          }
-          if (s < 3 && RD > MF) __builtin_amdgcn_sched_group_barrier(0x100, RD - MF, 0);
-        }
-#endif
       }
     }
   };
 
-  // ---- main loop: one barrier per K step, double-buffered LDS, loads
-  // kPrefetch steps ahead in as many register sets.  Unrolled by kPrefetch so
-  // register sets are compile-time indices; trailing iterations past the last
-  // step store and load (clamped) but do not compute.
+  // ---- main loop: one barrier per K step, double-buffered LDS, loads two
+  // steps ahead in two register sets.  Unrolled by two so register sets are
+  // compile-time indices; a trailing iteration past the last step stores and
+  // loads (clamped) but does not compute.
   using S0 = std::integral_constant<int, 0>;
   using S1 = std::integral_constant<int, 1>;
-  using S2 = std::integral_constant<int, 2>;
   auto main_loop = [&](auto ml_c) {
     auto iter = [&](int step, auto set_next) {
-      // data of step+1 sits in register set (step+1) % kPrefetch == set_next
+      // data of step+1 sits in register set (step+1) % 2 == set_next
       if (step < n_steps) compute(step & 1, ml_c);
       store((step + 1) & 1, set_next);
       load(step + 1 + kPrefetch, set_next);
       __syncthreads();
     };
-    if constexpr (kPrefetch == 2) {
-      load(0, S0{});
-      load(1, S1{});
-      store(0, S0{});
-      load(2, S0{});
-      __syncthreads();
-      for (int step = 0; step < n_steps; step += 2) {
-        iter(step, S1{});
-        iter(step + 1, S0{});
-      }
-    } else {
-      load(0, S0{});
-      load(1, S1{});
-      load(2, S2{});
-      store(0, S0{});
-      load(3, S0{});
-      __syncthreads();
-      for (int step = 0; step < n_steps; step += 3) {
-        iter(step, S1{});
-        iter(step + 1, S2{});
-        iter(step + 2, S0{});
-      }
+    load(0, S0{});
+    load(1, S1{});
+    store(0, S0{});
+    load(2, S0{});
+    __syncthreads();
+    for (int step = 0; step < n_steps; step += 2) {
+      iter(step, S1{});
+      iter(step + 1, S0{});
     }
   };
   static_assert(MB <= 8, "row blocks per wave");
@@ -455,22 +423,36 @@ __global__ __launch_bounds__(WM* WN * 64) void grouped_gemm_kernel(GemmArgs g) {
 }
 
 // ---------------------------------------------------------------------------
-// Prefill kernel with direct global -> LDS loads (global_load_lds_dwordx4) for
-// formats whose operands are staged as stored (BF16 both projections, FP8
-// down projection).  Per-thread ds_write staging costs about as much LDS time
-// as all the fragment reads of a step on this part; the direct loads move
-// each 16-byte chunk from L1 into LDS without passing through VGPRs.
+// Prefill kernel with direct global -> LDS loads (global_load_lds_dwordx4).
+// Per-thread ds_write staging costs about as much LDS time as all the
+// fragment reads of a K step on this part; direct loads move each 16-byte
+// chunk from L1 into LDS without passing through VGPRs.  Operands are staged
+// as stored: bf16 / fp16 / E4M3 activations, and bf16, E4M3 or packed E2M1
+// weight codes (with their E4M3 block scales); codes are expanded per lane
+// when the MFMA fragments are formed.
 //
-// LDS holds NBUF buffers of [BM + BN] rows x 128 bytes (one K step), with no
-// padding: the 16-byte chunk c of row r sits in slot c ^ ((r >> 1) & 7), so
-// the 16 rows a quarter-wave ds_read_b128 touches at one chunk land on 16
-// distinct 4-bank groups.  A direct load writes one wave's 64 x 16 bytes to
-// consecutive LDS addresses (8 rows); each lane fetches the global chunk that
+// LDS holds NBUF buffers of one K step: BM activation rows of 128 bytes, BN
+// weight rows of RB bytes (128 bf16 / fp8, 64 fp8 codes expanded to bf16, 32
+// packed E2M1), and for NVFP4 BN rows of 4 block-scale bytes.  Rows are not
+// padded: chunk c (16 bytes) of row r sits in slot c ^ ((r / (256 / RB)) %
+// (RB / 16)), so the 16 rows that a quarter-wave ds_read_b128 touches at one
+// chunk land on distinct banks.  A direct load writes one wave's 64 x 16
+// bytes to consecutive LDS addresses; each lane fetches the global chunk that
 // belongs in its slot.  Loads run NBUF - 1 steps ahead; at the top of each
 // step a wave waits for its own loads of that step (vmcnt) and the workgroup
 // meets at a barrier, after which every wave's loads are visible.
+//
+// K order inside a step: BF16 and FP8 feed the MFMA in natural order.  For
+// the expanded formats lane half lk takes the step's K range [32 lk, 32 lk +
+// 32) and sub-step s its 8 values at 32 lk + 8 s, so one lane's codes are
+// contiguous; activations are read in the same order (a permutation of K
+// inside the step, which the exact products and fp32 sums do not notice
+// beyond summation order).
 
-__device__ __forceinline__ int lds_swz(int r) { return (r >> 1) & 7; }
+template <int RB>
+__device__ __forceinline__ int lds_swz(int r) {
+  return (r / (256 / RB)) % (RB / 16);
+}
 
 // s_waitcnt immediate that waits until at most n vector memory operations of
 // this wave are outstanding (expcnt and lgkmcnt left at their maxima)
@@ -478,17 +460,23 @@ constexpr int vmcnt_imm(int n) { return (n & 15) | (7 << 4) | (15 << 8) | ((n >>
 
 template <int FMT, int STAGE, int BM, int BN, int WM, int WN, int NBUF>
 __global__ __launch_bounds__(WM* WN * 64) void grouped_gemm_dma_kernel(GemmArgs g) {
-  static_assert(FMT == kBF16 || FMT == kFP8, "operands staged as stored");
   static_assert(NBUF >= 2 && NBUF <= 4, "buffers");
   constexpr int NW = WM * WN;
   constexpr int WTM = BM / WM, WTN = BN / WN;
   constexpr int MB = WTM / 32, NB = WTN / 32;
-  constexpr int ESZ = (FMT == kFP8) ? 1 : 2;
-  constexpr int QA = BM / 8 / NW, QB = BN / 8 / NW;  // direct loads per wave per step
-  static_assert(QA * NW * 8 == BM && QB * NW * 8 == BN, "tile rows per wave");
-  static_assert(BM % 16 == 0, "swizzle period");
-  constexpr int DPS = QA + QB;  // vector memory operations per wave per step
-  constexpr int BUF = (BM + BN) * 128;
+  constexpr bool EXPAND = (FMT == kFP8X || FMT == kNVFP4);
+  constexpr int AESZ = (FMT == kFP8) ? 1 : 2;           // activation bytes per element
+  constexpr int KS = 128 / AESZ;                         // K elements per step
+  constexpr int RB = (FMT == kFP8X) ? 64 : (FMT == kNVFP4 ? 32 : 128);  // weight row bytes per step
+  constexpr int WB = (FMT == kNVFP4) ? 2 : 1;            // weight codes: 1/WB bytes per element
+  constexpr int NA = BM / 8;                             // activation loads per step (8 rows each)
+  constexpr int NBL = BN * RB / 1024;                    // weight loads per step
+  constexpr int NSC = (FMT == kNVFP4) ? BN / 64 : 0;     // scale loads per step (4 bytes x 64 rows)
+  constexpr int QA = (NA + NW - 1) / NW, QB = (NBL + NW - 1) / NW, QS = (NSC + NW - 1) / NW;
+  constexpr int DPS = QA + QB + QS;                      // vector memory operations per wave per step
+  constexpr int A_OFF = 0, B_OFF = BM * 128, S_OFF = BM * 128 + BN * RB;
+  constexpr int BUF = S_OFF + (FMT == kNVFP4 ? BN * 4 : 0);
+  static_assert(NA * 8 == BM && NBL * 1024 == BN * RB && BM % 16 == 0 && BN % 64 == 0, "tile");
   __shared__ __attribute__((aligned(1024))) uint8_t lds0[BUF];
   __shared__ __attribute__((aligned(1024))) uint8_t lds1[BUF];
   __shared__ __attribute__((aligned(1024))) uint8_t lds2[NBUF >= 3 ? BUF : 1024];
@@ -519,16 +507,20 @@ __global__ __launch_bounds__(WM* WN * 64) void grouped_gemm_dma_kernel(GemmArgs 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave / WN, wn = wave % WN;
   const int K = g.K, N = g.N;
-  const int k_bytes = K * ESZ;
-  const int n_steps = (k_bytes + 127) / 128;
+  const int a_bytes = K * AESZ;                 // activation row bytes
+  const int w_bytes = (FMT == kBF16) ? 2 * K : K / WB;  // weight row bytes
+  const int n_steps = (K + KS - 1) / KS;
 
-  // ---- per-lane global sources of the direct loads (fixed over K)
+  // ---- per-lane global sources of the direct loads (fixed over K).  When a
+  // load class has fewer instructions than waves, waves repeat one (same
+  // source, same LDS bytes) so every wave issues DPS loads per step.
   const uint8_t* a_src[QA];
-  int a_cof[QA];
+  int a_dst[QA], a_cof[QA];
 #pragma unroll
   for (int q = 0; q < QA; ++q) {
-    const int r = (wave + q * NW) * 8 + (lane >> 3);
-    const int c = (lane & 7) ^ lds_swz(r);
+    const int qi = (wave + q * NW) % NA;
+    const int r = qi * 8 + (lane >> 3);
+    const int c = (lane & 7) ^ lds_swz<128>(r);
     const int rr = min(r, rows_valid - 1);
     size_t src;
     if constexpr (STAGE == 0) {
@@ -536,41 +528,63 @@ __global__ __launch_bounds__(WM* WN * 64) void grouped_gemm_dma_kernel(GemmArgs 
     } else {
       src = static_cast<size_t>(row0 + rr);
     }
-    a_src[q] = static_cast<const uint8_t*>(g.a) + src * k_bytes + c * 16;
+    a_src[q] = static_cast<const uint8_t*>(g.a) + src * a_bytes + c * 16;
+    a_dst[q] = A_OFF + qi * 1024;
     a_cof[q] = c * 16;
   }
+  constexpr int CPR = RB / 16;  // 16-byte chunks per weight row and step
   const uint8_t* b_src[QB];
-  int b_cof[QB];
+  int b_dst[QB], b_cof[QB];
 #pragma unroll
   for (int q = 0; q < QB; ++q) {
-    const int r = (wave + q * NW) * 8 + (lane >> 3);
-    const int c = (lane & 7) ^ lds_swz(r);
+    const int qi = (wave + q * NW) % NBL;
+    const int r = qi * (1024 / RB) + lane / CPR;
+    const int c = (lane % CPR) ^ lds_swz<RB>(r);
     const int n = min(n0 + r, N - 1);
-    b_src[q] = static_cast<const uint8_t*>(g.b) + (static_cast<size_t>(e) * N + n) * k_bytes + c * 16;
+    b_src[q] = static_cast<const uint8_t*>(g.b) + (static_cast<size_t>(e) * N + n) * w_bytes + c * 16;
+    b_dst[q] = B_OFF + qi * 1024;
     b_cof[q] = c * 16;
+  }
+  const uint8_t* s_src[QS > 0 ? QS : 1];
+  int s_dst[QS > 0 ? QS : 1];
+  if constexpr (QS > 0) {
+#pragma unroll
+    for (int q = 0; q < QS; ++q) {
+      const int qi = (wave + q * NW) % NSC;
+      const int n = min(n0 + qi * 64 + lane, N - 1);
+      s_src[q] = g.b_bs + (static_cast<size_t>(e) * N + n) * (K / 16);
+      s_dst[q] = S_OFF + qi * 256;
+    }
   }
 
   // issue the direct loads of one K step into buffer buf.  Steps past the end
-  // re-read the last step (the buffer is not read again); a chunk past the
+  // re-read the last step (that buffer is not read again); a chunk past the
   // FP8 K tail reads the in-range chunk 64 bytes earlier and is zeroed when
   // the fragments are formed.
   auto dma = [&](int step_in, uint8_t* buf) {
     const int step = min(step_in, n_steps - 1);
-    const int kb = step * 128;
+    const int kb = step * 128;                 // activation bytes before this step
 #pragma unroll
     for (int q = 0; q < QA; ++q) {
       const uint8_t* p = a_src[q] + kb;
-      if constexpr (FMT == kFP8) p = (kb + a_cof[q] >= k_bytes) ? p - 64 : p;
-      __builtin_amdgcn_global_load_lds(
-          p, (__attribute__((address_space(3))) void*)(buf + (wave + q * NW) * 1024), 16, 0, 0);
+      if constexpr (FMT == kFP8) p = (kb + a_cof[q] >= a_bytes) ? p - 64 : p;
+      __builtin_amdgcn_global_load_lds(p, (__attribute__((address_space(3))) void*)(buf + a_dst[q]),
+                                       16, 0, 0);
     }
+    const int wb = step * RB;                  // weight bytes before this step
 #pragma unroll
     for (int q = 0; q < QB; ++q) {
-      const uint8_t* p = b_src[q] + kb;
-      if constexpr (FMT == kFP8) p = (kb + b_cof[q] >= k_bytes) ? p - 64 : p;
-      __builtin_amdgcn_global_load_lds(
-          p, (__attribute__((address_space(3))) void*)(buf + BM * 128 + (wave + q * NW) * 1024),
-          16, 0, 0);
+      const uint8_t* p = b_src[q] + wb;
+      if constexpr (FMT == kFP8) p = (wb + b_cof[q] >= w_bytes) ? p - 64 : p;
+      __builtin_amdgcn_global_load_lds(p, (__attribute__((address_space(3))) void*)(buf + b_dst[q]),
+                                       16, 0, 0);
+    }
+    if constexpr (QS > 0) {
+#pragma unroll
+      for (int q = 0; q < QS; ++q)
+        __builtin_amdgcn_global_load_lds(s_src[q] + step * 4,
+                                         (__attribute__((address_space(3))) void*)(buf + s_dst[q]),
+                                         4, 0, 0);
     }
   };
 
@@ -594,26 +608,65 @@ __global__ __launch_bounds__(WM* WN * 64) void grouped_gemm_dma_kernel(GemmArgs 
   const int lrow = lane & 31;
   const int lk = lane >> 5;
   // byte offsets of this lane's rows inside a buffer, and their swizzles
-  int a_row[MB], a_sw[MB], b_row[NB], b_sw[NB];
+  int a_row[MB], a_sw[MB], b_row[NB], b_sw[NB], s_row[NB];
 #pragma unroll
   for (int i = 0; i < MB; ++i) {
     const int r = (i * WM + wm) * 32 + lrow;
-    a_row[i] = r * 128;
-    a_sw[i] = lds_swz(r);
+    a_row[i] = A_OFF + r * 128;
+    a_sw[i] = lds_swz<128>(r);
   }
 #pragma unroll
   for (int j = 0; j < NB; ++j) {
     const int r = wn * WTN + j * 32 + lrow;
-    b_row[j] = BM * 128 + r * 128;
-    b_sw[j] = lds_swz(r);
+    b_row[j] = B_OFF + r * RB;
+    b_sw[j] = lds_swz<RB>(r);
+    s_row[j] = S_OFF + r * 4;
   }
+
+  using frag = std::conditional_t<FMT == kNVFP4, f16x8, bf16x8>;
+  // weight fragments of one lane for the 4 sub-steps of a step (expanded formats)
+  auto weight_frags = [&](const uint8_t* buf, int j, frag (&out)[4]) {
+    if constexpr (FMT == kFP8X) {
+      // 32 E4M3 codes at K 32 lk .. 32 lk + 31 -> bf16 (unit scale: exact)
+      const u32x4 x0 = *reinterpret_cast<const u32x4*>(buf + b_row[j] + (((2 * lk) ^ b_sw[j]) << 4));
+      const u32x4 x1 = *reinterpret_cast<const u32x4*>(buf + b_row[j] + (((2 * lk + 1) ^ b_sw[j]) << 4));
+      const uint32_t w[8] = {x0[0], x0[1], x0[2], x0[3], x1[0], x1[1], x1[2], x1[3]};
+#pragma unroll
+      for (int s = 0; s < 4; ++s) {
+        const bf16x2 p0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w[2 * s], 1.0f, false);
+        const bf16x2 p1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w[2 * s], 1.0f, true);
+        const bf16x2 p2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w[2 * s + 1], 1.0f, false);
+        const bf16x2 p3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w[2 * s + 1], 1.0f, true);
+        out[s] = bf16x8{p0[0], p0[1], p1[0], p1[1], p2[0], p2[1], p3[0], p3[1]};
+      }
+    } else if constexpr (FMT == kNVFP4) {
+      // 32 E2M1 codes at K 32 lk .. 32 lk + 31 (element 2i in the low nibble)
+      // -> fp16 (unit scale), times their E4M3 block scales (exact in fp16)
+      const u32x4 x = *reinterpret_cast<const u32x4*>(buf + b_row[j] + ((lk ^ b_sw[j]) << 4));
+      // the lane's two block scales (bytes 2 lk, 2 lk + 1 of the row's four);
+      // every E4M3 value is exact in fp16
+      const uint32_t sc4 = *reinterpret_cast<const uint32_t*>(buf + s_row[j]);
+      const f16x2 scs = lk ? __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(sc4, 1.0f, true)
+                           : __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(sc4, 1.0f, false);
+#pragma unroll
+      for (int s = 0; s < 4; ++s) {
+        const _Float16 sc = s < 2 ? scs[0] : scs[1];
+        const f16x2 s2 = {sc, sc};
+        const f16x2 p0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(x[s], 1.0f, 0) * s2;
+        const f16x2 p1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(x[s], 1.0f, 1) * s2;
+        const f16x2 p2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(x[s], 1.0f, 2) * s2;
+        const f16x2 p3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(x[s], 1.0f, 3) * s2;
+        out[s] = f16x8{p0[0], p0[1], p1[0], p1[1], p2[0], p2[1], p3[0], p3[1]};
+      }
+    }
+  };
 
   auto compute = [&](const uint8_t* buf, int step, auto ml_c) {
     constexpr int ML = decltype(ml_c)::value;
     if constexpr (ML > 0) {
       if constexpr (FMT == kFP8) {
         // the second 64-byte half of the last step lies past K when K % 128 == 64
-        const bool tail = (step * 128 + 64 >= k_bytes);
+        const bool tail = (step * 128 + 64 >= a_bytes);
 #pragma unroll
         for (int s = 0; s < 2; ++s) {  // 64 K per MFMA: chunks 4s + 2lk, +1
           i32x8 af[ML], bfr[NB];
@@ -643,6 +696,27 @@ __global__ __launch_bounds__(WM* WN * 64) void grouped_gemm_dma_kernel(GemmArgs 
             for (int j = 0; j < NB; ++j)
               acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
                   af[i], bfr[j], acc[i][j], 0, 0, 0, 127, 0, 127);
+        }
+      } else if constexpr (EXPAND) {
+        frag bx[NB][4];
+#pragma unroll
+        for (int j = 0; j < NB; ++j) weight_frags(buf, j, bx[j]);
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {  // K 32 lk + 8 s .. + 8: activation chunk 4 lk + s
+          const int c = lk * 4 + s;
+          frag af[ML];
+#pragma unroll
+          for (int i = 0; i < ML; ++i)
+            af[i] = *reinterpret_cast<const frag*>(buf + a_row[i] + ((c ^ a_sw[i]) << 4));
+#pragma unroll
+          for (int i = 0; i < ML; ++i)
+#pragma unroll
+            for (int j = 0; j < NB; ++j) {
+              if constexpr (FMT == kNVFP4)
+                acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af[i], bx[j][s], acc[i][j], 0, 0, 0);
+              else
+                acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bx[j][s], acc[i][j], 0, 0, 0);
+            }
         }
       } else {
 #pragma unroll
@@ -711,6 +785,7 @@ __global__ __launch_bounds__(WM* WN * 64) void grouped_gemm_dma_kernel(GemmArgs 
   // ---- epilogue (as in grouped_gemm_kernel)
   double scale = 1.0;
   if constexpr (FMT != kBF16) scale = static_cast<double>(g.a_s[0]) * static_cast<double>(g.b_s[e]);
+  float local_max = 0.f;
 #pragma unroll
   for (int i = 0; i < MB; ++i) {
     if (i >= ml) continue;
@@ -724,9 +799,12 @@ __global__ __launch_bounds__(WM* WN * 64) void grouped_gemm_dma_kernel(GemmArgs 
         if (rl < rows_valid && col < N) {
           const size_t at = static_cast<size_t>(row0 + rl) * N + col;
           if constexpr (STAGE == 0) {
-            static_assert(FMT == kBF16, "the FP8 up projection runs in grouped_gemm_kernel");
-            const double h = static_cast<double>(acc[i][j][r]);
-            static_cast<uint16_t*>(g.out)[at] = h > 0.0 ? f64_to_bf16(h * h) : static_cast<uint16_t>(0);
+            // a = bf16(relu(h)^2): h^2 is exact in double, so a is rounded once
+            double h = static_cast<double>(acc[i][j][r]);
+            if constexpr (FMT != kBF16) h *= scale;
+            const uint16_t b = h > 0.0 ? f64_to_bf16(h * h) : static_cast<uint16_t>(0);
+            static_cast<uint16_t*>(g.out)[at] = b;
+            if constexpr (FMT != kBF16) local_max = fmaxf(local_max, bf16_to_f32(b));
           } else {
             const float gate = g.row_gate[row0 + rl];
             float o;
@@ -741,6 +819,7 @@ __global__ __launch_bounds__(WM* WN * 64) void grouped_gemm_dma_kernel(GemmArgs 
       }
     }
   }
+  if constexpr (STAGE == 0 && FMT != kBF16) block_amax_to_slots(local_max, g.amax);
 }
 
 template <int FMT, int STAGE, int BM, int BN, int WM, int WN, int NBUF>
@@ -765,114 +844,50 @@ hipError_t launch_one(const GemmArgs& g, hipStream_t stream) {
   return hipGetLastError();
 }
 
-// Prefill tile shape (rows x columns, waves in M x N); kept as one switch so
-// alternative shapes can be compared by rebuilding with MOE_PREFILL_CFG.
-#ifndef MOE_PREFILL_CFG
-#define MOE_PREFILL_CFG 2
-#endif
-#if MOE_PREFILL_CFG == 0
-constexpr int kPBM = 128, kPBN = 128, kPWM = 2, kPWN = 2;
-#elif MOE_PREFILL_CFG == 1
-constexpr int kPBM = 128, kPBN = 256, kPWM = 2, kPWN = 2;
-#elif MOE_PREFILL_CFG == 2
-constexpr int kPBM = 128, kPBN = 128, kPWM = 2, kPWN = 4;
-#elif MOE_PREFILL_CFG == 3
-constexpr int kPBM = 256, kPBN = 128, kPWM = 4, kPWN = 2;
-#elif MOE_PREFILL_CFG == 4
-constexpr int kPBM = 64, kPBN = 256, kPWM = 1, kPWN = 4;
-#elif MOE_PREFILL_CFG == 5
-constexpr int kPBM = 128, kPBN = 256, kPWM = 2, kPWN = 4;
-#elif MOE_PREFILL_CFG == 6
-constexpr int kPBM = 128, kPBN = 384, kPWM = 2, kPWN = 6;
-#elif MOE_PREFILL_CFG == 7
-constexpr int kPBM = 64, kPBN = 384, kPWM = 1, kPWN = 6;
-#elif MOE_PREFILL_CFG == 8
-constexpr int kPBM = 128, kPBN = 192, kPWM = 2, kPWN = 3;
-#elif MOE_PREFILL_CFG == 9
-constexpr int kPBM = 64, kPBN = 256, kPWM = 2, kPWN = 4;
-#elif MOE_PREFILL_CFG == 10
-constexpr int kPBM = 256, kPBN = 256, kPWM = 4, kPWN = 2;
-#elif MOE_PREFILL_CFG == 11
-constexpr int kPBM = 256, kPBN = 128, kPWM = 4, kPWN = 2;
-#elif MOE_PREFILL_CFG == 12
-constexpr int kPBM = 128, kPBN = 256, kPWM = 2, kPWN = 2;
-#elif MOE_PREFILL_CFG == 13
-constexpr int kPBM = 128, kPBN = 256, kPWM = 1, kPWN = 4;
-#elif MOE_PREFILL_CFG == 14
-constexpr int kPBM = 256, kPBN = 256, kPWM = 2, kPWN = 4;
-#elif MOE_PREFILL_CFG == 15
-constexpr int kPBM = 256, kPBN = 128, kPWM = 2, kPWN = 4;
-#elif MOE_PREFILL_CFG == 16
-constexpr int kPBM = 128, kPBN = 128, kPWM = 1, kPWN = 4;
-#elif MOE_PREFILL_CFG == 17
-constexpr int kPBM = 256, kPBN = 128, kPWM = 2, kPWN = 2;
-#elif MOE_PREFILL_CFG == 18
-constexpr int kPBM = 256, kPBN = 256, kPWM = 2, kPWN = 2;
-#elif MOE_PREFILL_CFG == 19
-constexpr int kPBM = 128, kPBN = 128, kPWM = 2, kPWN = 2;
-#elif MOE_PREFILL_CFG == 20
-constexpr int kPBM = 256, kPBN = 128, kPWM = 4, kPWN = 1;
-#else
-#error "unknown MOE_PREFILL_CFG"
-#endif
 
-// Direct-load prefill shape (MOE_DMA_CFG selects alternatives for comparison)
-#ifndef MOE_DMA_CFG
-#define MOE_DMA_CFG 0
-#endif
-#if MOE_DMA_CFG == 0
-constexpr int kDBM = 128, kDBN = 128, kDWM = 2, kDWN = 4, kDBUF = 2;
-#elif MOE_DMA_CFG == 1
-constexpr int kDBM = 128, kDBN = 128, kDWM = 2, kDWN = 4, kDBUF = 3;
-#elif MOE_DMA_CFG == 2
-constexpr int kDBM = 128, kDBN = 128, kDWM = 2, kDWN = 2, kDBUF = 2;
-#elif MOE_DMA_CFG == 3
-constexpr int kDBM = 128, kDBN = 128, kDWM = 2, kDWN = 2, kDBUF = 3;
-#elif MOE_DMA_CFG == 4
-constexpr int kDBM = 128, kDBN = 256, kDWM = 2, kDWN = 4, kDBUF = 2;
-#elif MOE_DMA_CFG == 5
-constexpr int kDBM = 256, kDBN = 128, kDWM = 4, kDWN = 2, kDBUF = 2;
-#elif MOE_DMA_CFG == 6
-constexpr int kDBM = 128, kDBN = 256, kDWM = 2, kDWN = 4, kDBUF = 3;
-#elif MOE_DMA_CFG == 7
-constexpr int kDBM = 128, kDBN = 128, kDWM = 2, kDWN = 4, kDBUF = 4;
-#elif MOE_DMA_CFG == 8
-constexpr int kDBM = 64, kDBN = 128, kDWM = 2, kDWN = 4, kDBUF = 3;
-#elif MOE_DMA_CFG == 9
-constexpr int kDBM = 128, kDBN = 64, kDWM = 4, kDWN = 2, kDBUF = 3;
-#elif MOE_DMA_CFG == 10
-constexpr int kDBM = 64, kDBN = 128, kDWM = 1, kDWN = 4, kDBUF = 4;
-#elif MOE_DMA_CFG == 11
-constexpr int kDBM = 128, kDBN = 128, kDWM = 2, kDWN = 2, kDBUF = 4;
-#else
-#error "unknown MOE_DMA_CFG"
-#endif
+// Prefill tile of each format and projection for the direct-load kernel
+// (rows x columns, waves in M x N, LDS buffers), chosen by measurement on the
+// 4096-token batch: 128 x 128 tiles with eight 64 x 32 wave tiles and two
+// buffers (two workgroups per CU) for BF16 and the FP8 down projection, 128 x
+// 256 for the FP8 up projection (its weight rows are half as wide in LDS), and
+// four 64 x 64 wave tiles for NVFP4, which expands each weight fragment once
+// per wave.
+template <int FMT, int STAGE>
+struct PrefillTile {
+  static constexpr int BM = 128, BN = 128, WM = 2, WN = 4, NBUF = 2;
+};
+template <>
+struct PrefillTile<kFP8X, 0> {
+  static constexpr int BM = 128, BN = 256, WM = 2, WN = 4, NBUF = 2;
+};
+template <int STAGE>
+struct PrefillTile<kNVFP4, STAGE> {
+  static constexpr int BM = 128, BN = 128, WM = 2, WN = 2, NBUF = 2;
+};
 
-// prefill projections whose operands are staged as stored use the direct-load kernel
-constexpr bool uses_dma(int fmt, int stage) {
-  return fmt == kBF16 || (fmt == kFP8 && stage == 1);
-}
+// decode batches: 32-row tiles in the register-staged kernel
+constexpr int kDecodeRows = 32;
+constexpr int kDecodeMaxT = 512;
 
 template <int FMT, int STAGE>
 hipError_t launch_fmt_stage(int T, const GemmArgs& g, hipStream_t stream) {
-  const GemmShape s = gemm_shape(FMT == kFP8X ? kFP8 : FMT, STAGE, T);
-  if (s.bm == 32) return launch_one<FMT, STAGE, 32, 128, 1, 4>(g, stream);
-  if constexpr (FMT == kBF16 || (FMT == kFP8 && STAGE == 1))
-    return launch_dma<FMT, STAGE, kDBM, kDBN, kDWM, kDWN, kDBUF>(g, stream);
-#if MOE_PREFILL_CFG == 2
-  // NVFP4 expands its weight codes in registers: 64x64 wave tiles (four waves)
-  // measured faster than 64x32 ones for both projections
-  if constexpr (FMT == kNVFP4) return launch_one<FMT, STAGE, 128, 128, 2, 2>(g, stream);
-#endif
-  return launch_one<FMT, STAGE, kPBM, kPBN, kPWM, kPWN>(g, stream);
+  if (T < kDecodeMaxT) return launch_one<FMT, STAGE, kDecodeRows, 128, 1, 4>(g, stream);
+  using P = PrefillTile<FMT, STAGE>;
+  return launch_dma<FMT, STAGE, P::BM, P::BN, P::WM, P::WN, P::NBUF>(g, stream);
 }
 
 }  // namespace
 
 GemmShape gemm_shape(int fmt, int stage, int T) {
-  if (T < 512) return GemmShape{32, 128};
-  if (uses_dma(fmt, stage)) return GemmShape{kDBM, kDBN};
-  return GemmShape{kPBM, kPBN};
+  if (T < kDecodeMaxT) return GemmShape{kDecodeRows, 128};
+  // every prefill tile is 128 rows high
+  static_assert(PrefillTile<kBF16, 0>::BM == 128 && PrefillTile<kBF16, 1>::BM == 128 &&
+                    PrefillTile<kFP8X, 0>::BM == 128 && PrefillTile<kFP8, 1>::BM == 128 &&
+                    PrefillTile<kNVFP4, 0>::BM == 128 && PrefillTile<kNVFP4, 1>::BM == 128,
+                "one prefill tile height");
+  (void)fmt;
+  (void)stage;
+  return GemmShape{PrefillTile<kBF16, 0>::BM, PrefillTile<kBF16, 0>::BN};
 }
 
 hipError_t launch_gemm(int fmt, int stage, int T, const GemmArgs& g, hipStream_t stream) {
