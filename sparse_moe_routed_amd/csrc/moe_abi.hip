@@ -4,9 +4,11 @@
 #include <stdint.h>
 #include <string.h>
 
+#include <algorithm>
 #include <limits>
 
 #include "../../include/moe.h"
+
 #include "moe_common.h"
 #include "moe_internal.h"
 
@@ -128,8 +130,10 @@ int32_t moe_workspace_layout(const moe_dims* dims, int32_t fmt, int32_t T, moe_w
 
 size_t moe_route_workspace_size(const moe_dims* dims, int32_t max_tokens) {
   if (!dims_ok(dims) || max_tokens < 0 || max_tokens > kMaxTokens) return 0;
-  const size_t bytes = static_cast<size_t>(moe::router_k_slices(1, dims->hidden)) *
-                       static_cast<size_t>(max_tokens) * dims->n_experts * 4;
+  const int slices = std::max(moe::router_k_slices(1, dims->hidden),
+                              moe::router_k_slices(1 << 20, dims->hidden));
+  const size_t bytes = static_cast<size_t>(slices) * static_cast<size_t>(max_tokens) *
+                       dims->n_experts * 4;
   return bytes < kAlign ? kAlign : (bytes + kAlign - 1) / kAlign * kAlign;
 }
 

@@ -17,7 +17,8 @@
 // batches over more CUs); waves keep several K steps of loads in flight.
 // Partial logits go to the workspace as [S, T, E] fp32.
 // router_topk_kernel: one wave per token sums the S partials in order, adds
-// the bias, selects the top k (ties to the lower index) and writes the gates.
+// the bias and takes k rounds of wave-wide maximum (DPP reductions, ties to
+// the lower index), then writes the renormalised softmax gates.
 #include "moe_common.h"
 #include "moe_internal.h"
 
@@ -118,24 +119,50 @@ __global__ __launch_bounds__(256) void router_logits_kernel(const uint16_t* __re
   }
 }
 
+// Largest 32-bit unsigned value over the wave, in every lane.  DPP row shifts
+// reduce each 16-lane row into its lane 15, two row broadcasts combine the
+// rows into lane 63; zero (the identity) fills lanes a shift leaves empty.
+__device__ __forceinline__ uint32_t wave_umax(uint32_t v) {
+  v = max(v, static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(v), 0x111, 0xf, 0xf, false)));
+  v = max(v, static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(v), 0x112, 0xf, 0xf, false)));
+  v = max(v, static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(v), 0x114, 0xf, 0xf, false)));
+  v = max(v, static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(v), 0x118, 0xf, 0xf, false)));
+  v = max(v, static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(v), 0x142, 0xa, 0xf, false)));
+  v = max(v, static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(v), 0x143, 0xc, 0xf, false)));
+  return static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(v), 63));
+}
+
+// order-preserving unsigned key of a float (larger float -> larger key; -inf
+// maps above 0, which marks an empty slot)
+__device__ __forceinline__ uint32_t float_key(float f) {
+  const uint32_t u = __float_as_uint(f);
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+// One wave per token: lane l holds experts l + 64 i.  Each of the k rounds
+// takes the largest key over the wave, then the lowest expert index holding
+// it (ballots over the slots in index order), and retires that expert.
+// Gates: z_j = exp(l_j - l_0), summed in slot order, g_j = z_j / sum.
 __global__ __launch_bounds__(256) void router_topk_kernel(const float* __restrict__ part,
                                                           const float* __restrict__ bias, int T,
                                                           int E, int S, int k,
                                                           int32_t* __restrict__ ids,
                                                           float* __restrict__ gates) {
   const int lane = threadIdx.x & 63;
-  const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (t >= T) return;
+  const int t = blockIdx.x * kWavesPerWg + (threadIdx.x >> 6);
+  if (t >= T) return;  // whole waves; no barriers below
   float v[kMaxE / 64];
+  uint32_t key[kMaxE / 64];
 #pragma unroll
   for (int i = 0; i < kMaxE / 64; ++i) {
     const int e = lane + 64 * i;
+    v[i] = -INFINITY;
+    key[i] = 0u;
     if (e < E) {
       float l = 0.f;
       for (int s = 0; s < S; ++s) l += part[(static_cast<size_t>(s) * T + t) * E + e];
       v[i] = l + (bias ? bias[e] : 0.f);
-    } else {
-      v[i] = -INFINITY;
+      key[i] = float_key(v[i]);
     }
   }
   float sel_v[8];
@@ -145,24 +172,26 @@ __global__ __launch_bounds__(256) void router_topk_kernel(const float* __restric
     sel_v[j] = 0.f;
     sel_i[j] = 0;
     if (j >= k) continue;
-    float bv = -INFINITY;
-    int bi = 0x7fffffff;
+    uint32_t m = key[0];
+#pragma unroll
+    for (int i = 1; i < kMaxE / 64; ++i) m = max(m, key[i]);
+    const uint32_t best = wave_umax(m);
+    int win = -1;
 #pragma unroll
     for (int i = 0; i < kMaxE / 64; ++i) {
-      const int e = lane + 64 * i;
-      if (e < E && (v[i] > bv || (v[i] == bv && e < bi))) { bv = v[i]; bi = e; }
+      const uint64_t b = __ballot(key[i] == best && key[i] != 0u);
+      if (win < 0 && b) win = 64 * i + __ffsll(static_cast<unsigned long long>(b)) - 1;
     }
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) {
-      const float ov = __shfl_xor(bv, o);
-      const int oi = __shfl_xor(bi, o);
-      if (ov > bv || (ov == bv && oi < bi)) { bv = ov; bi = oi; }
-    }
-    sel_v[j] = bv;
-    sel_i[j] = bi;
+    // the winner's logit, from the lane that holds it
+    float wv = -INFINITY;
 #pragma unroll
     for (int i = 0; i < kMaxE / 64; ++i)
-      if (lane + 64 * i == bi) v[i] = -INFINITY;  // remove the winner
+      if (lane + 64 * i == win) {
+        wv = v[i];
+        key[i] = 0u;
+      }
+    sel_v[j] = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, wv), win & 63));
+    sel_i[j] = win;
   }
   if (lane == 0) {
     const float m = sel_v[0];
@@ -186,10 +215,12 @@ __global__ __launch_bounds__(256) void router_topk_kernel(const float* __restric
 }  // namespace
 
 // K slices: each wave's K loop is a chain of L2 round trips, so the router
-// splits K four ways at every batch size (more waves in flight, shorter chains)
-int router_k_slices(int /*T*/, int H) {
-  int S = 4;
-  while (S > 1 && H % (32 * S)) S >>= 1;
+// splits K into slices of whole 32-element MFMA steps: up to 12 for small
+// batches (few token blocks to spread over the CUs), up to 4 otherwise.
+int router_k_slices(int T, int H) {
+  const int steps = H / 32;
+  int S = T <= 256 ? 12 : 4;
+  while (S > 1 && steps % S) --S;
   return S;
 }
 
@@ -215,8 +246,8 @@ hipError_t launch_router(const uint16_t* x, const uint16_t* w_packed, const floa
     hipLaunchKernelGGL(router_logits_kernel<4>, grid, dim3(256), 0, stream, x, w_packed, T, H, E,
                        S, part);
   }
-  hipLaunchKernelGGL(router_topk_kernel, dim3((T + 3) / 4), dim3(256), 0, stream, part, bias, T, E,
-                     S, k, ids, gates);
+  hipLaunchKernelGGL(router_topk_kernel, dim3((T + kWavesPerWg - 1) / kWavesPerWg), dim3(256), 0,
+                     stream, part, bias, T, E, S, k, ids, gates);
   return hipGetLastError();
 }
 
