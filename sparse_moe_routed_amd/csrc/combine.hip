@@ -15,20 +15,28 @@ namespace {
 
 constexpr int kCThreads = 256;
 
+// grid (T, G): workgroup (t, gy) sums column groups of four gy * kCThreads +
+// tid, stepping by G * kCThreads (G spreads a token over several workgroups
+// for small batches).  The K row loads of a group are issued together (a
+// dropped slot reads row 0 and is not added), then added in slot order.
+template <int K>
 __global__ __launch_bounds__(kCThreads) void combine_kernel(const float* __restrict__ rows,
                                                             const int32_t* __restrict__ inv,
-                                                            int k, int H, void* y, int y_f32) {
+                                                            int H, void* y, int y_f32) {
   const int t = blockIdx.x;
-  int src[8];
+  int src[K];
 #pragma unroll
-  for (int j = 0; j < 8; ++j) src[j] = j < k ? inv[static_cast<size_t>(t) * k + j] : -1;
+  for (int j = 0; j < K; ++j) src[j] = inv[static_cast<size_t>(t) * K + j];
   const int h4 = H / 4;
-  for (int c = threadIdx.x; c < h4; c += kCThreads) {
+  for (int c = blockIdx.y * kCThreads + threadIdx.x; c < h4; c += gridDim.y * kCThreads) {
+    f32x4 v[K];
+#pragma unroll
+    for (int j = 0; j < K; ++j)
+      v[j] = reinterpret_cast<const f32x4*>(rows + static_cast<size_t>(src[j] < 0 ? 0 : src[j]) * H)[c];
     f32x4 s = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      if (src[j] >= 0) s += reinterpret_cast<const f32x4*>(rows + static_cast<size_t>(src[j]) * H)[c];
-    }
+    for (int j = 0; j < K; ++j)
+      if (src[j] >= 0) s += v[j];
     if (y_f32) {
       reinterpret_cast<f32x4*>(static_cast<float*>(y) + static_cast<size_t>(t) * H)[c] = s;
     } else {
@@ -78,8 +86,21 @@ __global__ __launch_bounds__(kCThreads) void residual_kernel(uint16_t* __restric
 hipError_t launch_combine(const float* rows, const int32_t* inv, int T, int k, int H, void* y,
                           int y_f32, hipStream_t stream) {
   if (T <= 0) return hipSuccess;
-  hipLaunchKernelGGL(combine_kernel, dim3(T), dim3(kCThreads), 0, stream, rows, inv, k, H, y,
-                     y_f32);
+  // small batches: one column block per workgroup (a single round of loads);
+  // large batches: one workgroup per token
+  const int g = T < 512 ? (H / 4 + kCThreads - 1) / kCThreads : 1;
+  const dim3 grid(T, g);
+  switch (k) {
+#define MOE_COMBINE_K(KK)                                                                       \
+  case KK:                                                                                      \
+    hipLaunchKernelGGL(combine_kernel<KK>, grid, dim3(kCThreads), 0, stream, rows, inv, H, y, \
+                       y_f32);                                                                  \
+    break;
+    MOE_COMBINE_K(1) MOE_COMBINE_K(2) MOE_COMBINE_K(3) MOE_COMBINE_K(4)
+    MOE_COMBINE_K(5) MOE_COMBINE_K(6) MOE_COMBINE_K(7) MOE_COMBINE_K(8)
+#undef MOE_COMBINE_K
+    default: return hipErrorInvalidValue;
+  }
   return hipGetLastError();
 }
 
