@@ -171,7 +171,9 @@ def _forward_case(L, fmt, T, outliers=False, check_act=True):
     return y, y_ref
 
 
-@pytest.mark.parametrize("T", [1, 4, 64, 333])
+# 333 / 342: the last single-chunk and a two-chunk permutation with decode
+# tiles; 512: the first batch on the prefill tiles
+@pytest.mark.parametrize("T", [1, 4, 64, 333, 342, 512])
 def test_forward_bf16_full_shape(full, T):
     _forward_case(full, "bf16", T, outliers=T > 100)
 
@@ -186,6 +188,13 @@ def test_forward_small_shape(small, fmt, T):
 @pytest.mark.parametrize("T", [4, 64])
 def test_forward_quantised_full_shape(full, fmt, T):
     _forward_case(full, fmt, T)
+
+
+@pytest.mark.parametrize("fmt", ["fp8", "nvfp4"])
+def test_forward_quantised_prefill_t4096(full, fmt):
+    # the prefill kernels of the quantised formats at the full batch: every
+    # output element against the oracle (FP8: every intermediate too)
+    _forward_case(full, fmt, 4096)
 
 
 def test_forward_bf16_output_and_determinism(full):
