@@ -880,14 +880,14 @@ hipError_t launch_fmt_stage(int T, const GemmArgs& g, hipStream_t stream) {
 
 GemmShape gemm_shape(int fmt, int stage, int T) {
   if (T < kDecodeMaxT) return GemmShape{kDecodeRows, 128};
-  // every prefill tile is 128 rows high
-  static_assert(PrefillTile<kBF16, 0>::BM == 128 && PrefillTile<kBF16, 1>::BM == 128 &&
-                    PrefillTile<kFP8X, 0>::BM == 128 && PrefillTile<kFP8, 1>::BM == 128 &&
-                    PrefillTile<kNVFP4, 0>::BM == 128 && PrefillTile<kNVFP4, 1>::BM == 128,
-                "one prefill tile height");
-  (void)fmt;
-  (void)stage;
-  return GemmShape{PrefillTile<kBF16, 0>::BM, PrefillTile<kBF16, 0>::BN};
+  switch (fmt * 2 + stage) {
+    case kBF16 * 2 + 0: return GemmShape{PrefillTile<kBF16, 0>::BM, PrefillTile<kBF16, 0>::BN};
+    case kBF16 * 2 + 1: return GemmShape{PrefillTile<kBF16, 1>::BM, PrefillTile<kBF16, 1>::BN};
+    case kFP8 * 2 + 0: return GemmShape{PrefillTile<kFP8X, 0>::BM, PrefillTile<kFP8X, 0>::BN};
+    case kFP8 * 2 + 1: return GemmShape{PrefillTile<kFP8, 1>::BM, PrefillTile<kFP8, 1>::BN};
+    case kNVFP4 * 2 + 0: return GemmShape{PrefillTile<kNVFP4, 0>::BM, PrefillTile<kNVFP4, 0>::BN};
+    default: return GemmShape{PrefillTile<kNVFP4, 1>::BM, PrefillTile<kNVFP4, 1>::BN};
+  }
 }
 
 hipError_t launch_gemm(int fmt, int stage, int T, const GemmArgs& g, hipStream_t stream) {
