@@ -19,6 +19,7 @@ pytestmark = pytest.mark.gpu
 TOL = {"bf16": 2e-2, "fp8": 5e-2, "nvfp4": 1e-1}
 FULL = synth.Dims()
 SMALL = synth.Dims(hidden=256, ffn=192, n_experts=32, top_k=4)
+WIDE = synth.Dims(hidden=128, ffn=128, n_experts=256, top_k=8)  # largest E and k supported
 
 
 def _ld(d: synth.Dims) -> moe.LayerDims:
@@ -59,6 +60,11 @@ def full():
 @pytest.fixture(scope="module")
 def small():
     return Layer(SMALL, 0)
+
+
+@pytest.fixture(scope="module")
+def wide():
+    return Layer(WIDE, 0)
 
 
 def _x(T, dims, outliers=False):
@@ -184,6 +190,17 @@ def test_forward_small_shape(small, fmt, T):
     _forward_case(small, fmt, T)
 
 
+@pytest.mark.parametrize("fmt", ["bf16", "fp8", "nvfp4"])
+@pytest.mark.parametrize("T", [300, 600])
+def test_forward_max_experts_and_k(wide, fmt, T):
+    # 256 experts, 8 per token: router, permutation and both GEMM regimes
+    # (300 tokens: decode tiles; 600: prefill tiles)
+    ids_o, g_o, gap, ids_g, g_g = _route_both(wide, _x(T, WIDE))
+    same = np.array([sorted(a) == sorted(b) for a, b in zip(ids_g, ids_o)])
+    assert np.all(same | (gap < om.NEAR_TIE))
+    _forward_case(wide, fmt, T)
+
+
 @pytest.mark.parametrize("fmt", ["fp8", "nvfp4"])
 @pytest.mark.parametrize("T", [4, 64])
 def test_forward_quantised_full_shape(full, fmt, T):
@@ -259,6 +276,46 @@ def test_prefill_t4096_sampled_tokens(full):
     # every token hit exactly 6 distinct experts
     ia = ids_g.cpu().numpy()
     assert np.all(np.sort(ia, 1)[:, 1:] != np.sort(ia, 1)[:, :-1])
+
+
+def _sampled_forward_check(L, x, sample, fmt="bf16"):
+    # the library routes and runs the whole batch; the oracle checks a sample
+    # of tokens (each token's output depends only on its own routing)
+    xd = x.cuda()
+    ids_g, g_g = moe.route(xd, L.router)
+    y = moe.forward(xd, ids_g, g_g, L.bank(fmt))
+    torch.cuda.synchronize()
+    xs = x[torch.from_numpy(sample)].float().numpy()
+    ids_o, g_o, gap, _ = om.route(xs, L.w_r.numpy(), L.b.numpy(), L.dims.top_k)
+    ig = ids_g.cpu().numpy()[sample]
+    same = np.array([sorted(a) == sorted(b) for a, b in zip(ig, ids_o)])
+    assert np.all(same | (gap < om.NEAR_TIE))
+    y_ref = om.forward(xs, ids_o, g_o, L.oracle_bank(fmt).preload(np.unique(ids_o), 16))
+    err, _ = _rel_err(y.cpu().double().numpy()[sample][same], y_ref[same])
+    return err, ids_g.cpu().numpy()
+
+
+def test_forward_identical_tokens(full):
+    # degenerate routing: every token picks the same 6 experts, which then
+    # hold 2048 rows each (16 row tiles) while the other 122 get none
+    T = 2048
+    x = _x(1, FULL).repeat(T, 1)
+    sample = np.array([0, 1, 777, T - 1])
+    err, ids = _sampled_forward_check(full, x, sample)
+    _log(f"identical tokens: max|d|/rms = {err:.3e}")
+    assert err <= TOL["bf16"]
+    assert np.all(ids == ids[0])
+
+
+def test_forward_large_batch_sampled(full):
+    # 32768 tokens: 96 permutation chunks and the largest grids
+    T = 32768
+    x = _x(T, FULL)
+    rng = np.random.default_rng(1)
+    sample = np.unique(np.concatenate([rng.choice(T, 24, replace=False), [0, T - 1]]))
+    err, _ = _sampled_forward_check(full, x, sample)
+    _log(f"T={T} sample of {len(sample)}: max|d|/rms = {err:.3e}")
+    assert err <= TOL["bf16"]
 
 
 # --------------------------------------------------------------------------- quantisers
