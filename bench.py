@@ -87,8 +87,9 @@ def main():
     args = parse()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus > 1 or world > 1:
-        print(f"bench.py: this build measures one GPU only; --gpus {max(args.gpus, world)} "
-              "is not supported (the expert-parallel split is described in DESIGN.md)",
+        print(f"bench.py: measures one GPU only; --gpus {max(args.gpus, world)} "
+              "is not supported (the layer would shard by expert parallelism; only the "
+              "single-GPU kernels are built)",
               file=sys.stderr)
         sys.exit(2)
 

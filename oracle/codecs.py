@@ -12,12 +12,14 @@ Encoders round to nearest, ties to even, and saturate finite values to the
 largest magnitude.  The sign bit of a code is set iff the input is < 0 (so a
 negative value that rounds to zero gives the negative-zero code).
 
-Quantisation recipes.  The pages fix only the formats: FP8 is "scalar-scale
-E4M3 W8A8" and the 4-bit experts are "W4A4" (bloomery issue #967, section 2
-"Checkpoint facts"; section 6 asks to keep each release's activation rules).
-The block size (16), the E4M3 block scale and the fp32 tensor scale of the
-4-bit format, and the dynamic per-tensor activation scale, are readings of
-the layer description (recorded in the design doc).  Every step is a named IEEE
+Quantisation recipes.  The pages fix only the formats: FP8 experts use E4M3
+codes with one scalar scale for weights and activations (W8A8), and the
+4-bit experts quantise weights and activations alike (W4A4) (bloomery issue
+#967, section 2 "Checkpoint facts"; section 6 keeps each release's
+activation rules).  The block size (16), the E4M3 block scale and the fp32
+tensor scale of the 4-bit format, and the dynamic per-tensor activation
+scale, are readings of the layer description, chosen as the plainest ones
+consistent with it.  Every step is a named IEEE
 float32 operation so that two independent implementations reach identical
 codes from identical inputs:
 

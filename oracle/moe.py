@@ -28,7 +28,8 @@ Parity status:
   quantised paths  pinned through the codec pins plus exact all-ones and
                    representable-value round trips
   prenorm/stack    prenorm pinned by closed form on constant rows; the stack
-                   is composition only (stacked path reading)
+                   is composition only (the pre-norm is a reading: the literal residual
+                   stack without normalisation diverges within a few layers)
 """
 from __future__ import annotations
 
