@@ -160,11 +160,16 @@ def main():
         if n_layers == 1:
             run_layer(layers[0], x0, evs[0] if evs else None)
         else:
+            # pre-norm, layer, then the residual fused with the next layer's
+            # pre-norm; the last layer ends with the plain residual
             xs.copy_(x0)
+            moe.prenorm(xs, xin)
             for li, L in enumerate(layers):
-                moe.prenorm(xs, xin)
                 run_layer(L, xin, evs[li] if evs else None)
-                moe.residual_add(xs, y)
+                if li + 1 < n_layers:
+                    moe.residual_prenorm(xs, y, xin)
+                else:
+                    moe.residual_add(xs, y)
 
     for _ in range(args.warmup):
         step()

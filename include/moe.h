@@ -210,11 +210,17 @@ int32_t moe_quantize_activation(int32_t fmt, int32_t rows, int32_t cols,
 /* Stacked-path helpers.  The pages' model normalises around its layers
  * (audio.cpp notes, section "Q4_K, Q3_K and Q2_K expert profiles": routing and
  * normalisation stay unchanged); a weightless RMS pre-norm is used:
- *   moe_prenorm:      out_t = bf16(x_t / sqrt(mean(x_t^2) + 1e-6))
- *   moe_residual_add: x_t   = bf16(x_t + y_t)
- * x, out [dev] bf16 [T, H]; y [dev] fp32 [T, H]. */
+ *   moe_prenorm:           out_t = bf16(x_t / sqrt(mean(x_t^2) + 1e-6))
+ *   moe_residual_add:      x_t   = bf16(x_t + y_t)
+ *   moe_residual_prenorm:  moe_residual_add, then moe_prenorm of the new x
+ *                          into out, in one pass (bit-identical to the two
+ *                          calls; for the step between stacked layers)
+ * x, out [dev] bf16 [T, H] (out must not be x); y [dev] fp32 [T, H];
+ * H % 64 == 0.  Row sums of squares are accumulated in double. */
 int32_t moe_prenorm(int32_t T, int32_t H, const void* x, void* out, void* stream);
 int32_t moe_residual_add(int32_t T, int32_t H, void* x, const float* y, void* stream);
+int32_t moe_residual_prenorm(int32_t T, int32_t H, void* x, const float* y, void* out,
+                             void* stream);
 
 #ifdef __cplusplus
 }

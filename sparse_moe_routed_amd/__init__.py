@@ -88,6 +88,8 @@ _SIGS = {
                                      ctypes.c_void_p, ctypes.c_void_p]),
     "moe_residual_add": (ctypes.c_int32, [ctypes.c_int32, ctypes.c_int32, ctypes.c_void_p,
                                           ctypes.c_void_p, ctypes.c_void_p]),
+    "moe_residual_prenorm": (ctypes.c_int32, [ctypes.c_int32, ctypes.c_int32, ctypes.c_void_p,
+                                              ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]),
 }
 
 _lib = None
@@ -352,3 +354,17 @@ def residual_add(x: torch.Tensor, y: torch.Tensor) -> torch.Tensor:
     _dev(y, torch.float32, "y", (T, H))
     _check("moe_residual_add", lib().moe_residual_add(T, H, _ptr(x), _ptr(y), _stream()))
     return x
+
+
+def residual_prenorm(x: torch.Tensor, y: torch.Tensor,
+                     out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """moe_residual_prenorm: x <- bf16(x + y) in place, returns prenorm(x) in out."""
+    T, H = x.shape
+    _dev(x, torch.bfloat16, "x")
+    _dev(y, torch.float32, "y", (T, H))
+    if out is None:
+        out = torch.empty_like(x)
+    _dev(out, torch.bfloat16, "out", (T, H))
+    _check("moe_residual_prenorm",
+           lib().moe_residual_prenorm(T, H, _ptr(x), _ptr(y), _ptr(out), _stream()))
+    return out

@@ -81,6 +81,37 @@ __global__ __launch_bounds__(kCThreads) void residual_kernel(uint16_t* __restric
     x[i] = f64_to_bf16(static_cast<double>(bf16_to_f32(x[i])) + static_cast<double>(y[i]));
 }
 
+// Between stacked layers: x = bf16(x + y), then out = bf16(x / sqrt(mean(x^2) +
+// 1e-6)) of the new x, one row per workgroup.  Same per-element arithmetic and
+// the same reduction order as residual_kernel followed by prenorm_kernel.
+__global__ __launch_bounds__(kCThreads) void residual_prenorm_kernel(uint16_t* __restrict__ x,
+                                                                     const float* __restrict__ y,
+                                                                     int H,
+                                                                     uint16_t* __restrict__ out) {
+  __shared__ double part[kCThreads / 64];
+  const int t = blockIdx.x;
+  uint16_t* xr = x + static_cast<size_t>(t) * H;
+  const float* yr = y + static_cast<size_t>(t) * H;
+  double ss = 0.0;
+  for (int c = threadIdx.x; c < H; c += kCThreads) {
+    const uint16_t xn = f64_to_bf16(static_cast<double>(bf16_to_f32(xr[c])) + static_cast<double>(yr[c]));
+    xr[c] = xn;
+    const double v = bf16_to_f32(xn);
+    ss += v * v;
+  }
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) ss += __shfl_xor(ss, o);
+  if ((threadIdx.x & 63) == 0) part[threadIdx.x >> 6] = ss;
+  __syncthreads();
+  double tot = 0.0;
+#pragma unroll
+  for (int w = 0; w < kCThreads / 64; ++w) tot += part[w];
+  const double d = sqrt(tot / static_cast<double>(H) + 1e-6);
+  uint16_t* o = out + static_cast<size_t>(t) * H;
+  for (int c = threadIdx.x; c < H; c += kCThreads)  // this thread wrote xr[c] above
+    o[c] = f64_to_bf16(static_cast<double>(bf16_to_f32(xr[c])) / d);
+}
+
 }  // namespace
 
 hipError_t launch_combine(const float* rows, const int32_t* inv, int T, int k, int H, void* y,
@@ -117,6 +148,13 @@ hipError_t launch_residual(uint16_t* x, const float* y, int T, int H, hipStream_
   if (g > 8192) g = 8192;
   hipLaunchKernelGGL(residual_kernel, dim3(static_cast<unsigned>(g)), dim3(kCThreads), 0, stream,
                      x, y, n);
+  return hipGetLastError();
+}
+
+hipError_t launch_residual_prenorm(uint16_t* x, const float* y, int T, int H, uint16_t* out,
+                                   hipStream_t stream) {
+  if (T <= 0) return hipSuccess;
+  hipLaunchKernelGGL(residual_prenorm_kernel, dim3(T), dim3(kCThreads), 0, stream, x, y, H, out);
   return hipGetLastError();
 }
 

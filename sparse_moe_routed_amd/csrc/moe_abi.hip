@@ -378,4 +378,14 @@ int32_t moe_residual_add(int32_t T, int32_t H, void* x, const float* y, void* st
                                          static_cast<hipStream_t>(stream)));
 }
 
+int32_t moe_residual_prenorm(int32_t T, int32_t H, void* x, const float* y, void* out,
+                             void* stream) {
+  if (T < 0 || T > kMaxTokens || H <= 0 || H % 64) return MOE_EINVAL;
+  if (!x || !y || !out || out == x) return MOE_EINVAL;
+  if (T == 0) return MOE_OK;
+  return hip_status(moe::launch_residual_prenorm(static_cast<uint16_t*>(x), y, T, H,
+                                                 static_cast<uint16_t*>(out),
+                                                 static_cast<hipStream_t>(stream)));
+}
+
 }  // extern "C"

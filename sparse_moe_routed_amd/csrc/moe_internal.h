@@ -94,5 +94,7 @@ hipError_t launch_quant_weights(int fmt, const uint16_t* w, int E, int N, int K,
 
 hipError_t launch_prenorm(const uint16_t* x, int T, int H, uint16_t* out, hipStream_t stream);
 hipError_t launch_residual(uint16_t* x, const float* y, int T, int H, hipStream_t stream);
+hipError_t launch_residual_prenorm(uint16_t* x, const float* y, int T, int H, uint16_t* out,
+                                   hipStream_t stream);
 
 }  // namespace moe

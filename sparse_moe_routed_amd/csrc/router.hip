@@ -12,10 +12,9 @@
 // x * part is exact in the fp32 accumulator of v_mfma_f32_16x16x32_bf16 and
 // the logits carry only fp32 summation error.
 //
-// router_logits_kernel: a workgroup computes 64 tokens against 16 (small
-// batches) or 64 experts over one of S slices of K (S > 1 spreads small
-// batches over more CUs); waves keep several K steps of loads in flight.
-// Partial logits go to the workspace as [S, T, E] fp32.
+// router_logits_kernel (T <= 256) and router_logits_lds_kernel (larger
+// batches) write partial logits of S slices of K to the workspace as [S, T, E]
+// fp32; more slices spread small batches over more CUs.
 // router_topk_kernel: one wave per token sums the S partials in order, adds
 // the bias and takes k rounds of wave-wide maximum (DPP reductions, ties to
 // the lower index), then writes the renormalised softmax gates.
@@ -47,47 +46,39 @@ __global__ __launch_bounds__(256) void router_pack_kernel(const float* __restric
   }
 }
 
-// TB = 16-token row blocks per wave.  TB == 1 (small batches): the 4 waves
-// take 4 row blocks of one 16-expert block.  TB == 4: each wave takes all 64
-// tokens of the workgroup against its own 16-expert block, reusing every
-// router fragment for 4 MFMA row blocks (less L2 traffic per logit).
-template <int TB>
+// Small batches: the 4 waves of a workgroup take 4 blocks of 16 tokens against
+// one 16-expert block over one K slice, loading MFMA fragments straight from
+// global memory with several K steps in flight (few tokens: latency-bound).
 __global__ __launch_bounds__(256) void router_logits_kernel(const uint16_t* __restrict__ x,
                                                             const uint16_t* __restrict__ wp,
                                                             int T, int H, int E, int S,
                                                             float* __restrict__ part) {
-  constexpr int U = TB == 1 ? 4 : 2;  // K steps of loads in flight
+  constexpr int U = 4;  // K steps of loads in flight
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
-  const int t0 = blockIdx.x * kTokPerWg + (TB == 1 ? wave * kTokPerWave : 0);
-  const int eb = TB == 1 ? blockIdx.y : blockIdx.y * kWavesPerWg + wave;
+  const int t0 = blockIdx.x * kTokPerWg + wave * kTokPerWave;
+  const int eb = blockIdx.y;
   if (t0 >= T || eb * 16 >= E) return;  // no barriers in this kernel
   const int s = blockIdx.z;
   const int row = lane & 15;       // MFMA row (token) / column (expert) of this lane
   const int kq = (lane >> 4) * 8;  // this lane's 8-wide K slice inside a 32-K step
   const int kbeg = s * (H / S), kend = kbeg + H / S;
   const size_t n = static_cast<size_t>(E) * H;
-  const uint16_t* xrow[TB];
-#pragma unroll
-  for (int b = 0; b < TB; ++b)
-    xrow[b] = x + static_cast<size_t>(min(t0 + b * 16 + row, T - 1)) * H + kq;
+  const uint16_t* xrow = x + static_cast<size_t>(min(t0 + row, T - 1)) * H + kq;
   const uint16_t* w_hi = wp + static_cast<size_t>(eb * 16 + row) * H + kq;
   const uint16_t* w_mid = w_hi + n;
   const uint16_t* w_lo = w_hi + 2 * n;
 
-  f32x4 acc[TB][U];
+  f32x4 acc[U];
 #pragma unroll
-  for (int b = 0; b < TB; ++b)
-#pragma unroll
-    for (int u = 0; u < U; ++u) acc[b][u] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int u = 0; u < U; ++u) acc[u] = f32x4{0.f, 0.f, 0.f, 0.f};
   for (int k0 = kbeg; k0 < kend; k0 += U * 32) {
-    bf16x8 a[U][TB], bh[U], bm[U], bl[U];
+    bf16x8 a[U], bh[U], bm[U], bl[U];
 #pragma unroll
     for (int u = 0; u < U; ++u) {  // issue the loads of U K steps first
       const int kk = k0 + u * 32;
       if (kk < kend) {
-#pragma unroll
-        for (int b = 0; b < TB; ++b) a[u][b] = *reinterpret_cast<const bf16x8*>(xrow[b] + kk);
+        a[u] = *reinterpret_cast<const bf16x8*>(xrow + kk);
         bh[u] = *reinterpret_cast<const bf16x8*>(w_hi + kk);
         bm[u] = *reinterpret_cast<const bf16x8*>(w_mid + kk);
         bl[u] = *reinterpret_cast<const bf16x8*>(w_lo + kk);
@@ -96,26 +87,126 @@ __global__ __launch_bounds__(256) void router_logits_kernel(const uint16_t* __re
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       if (k0 + u * 32 >= kend) break;
-#pragma unroll
-      for (int b = 0; b < TB; ++b) {
-        acc[b][u] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[u][b], bl[u], acc[b][u], 0, 0, 0);
-        acc[b][u] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[u][b], bm[u], acc[b][u], 0, 0, 0);
-        acc[b][u] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[u][b], bh[u], acc[b][u], 0, 0, 0);
-      }
+      acc[u] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[u], bl[u], acc[u], 0, 0, 0);
+      acc[u] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[u], bm[u], acc[u], 0, 0, 0);
+      acc[u] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[u], bh[u], acc[u], 0, 0, 0);
     }
   }
   // 16x16 f32 result: lane holds column (expert) lane%16, rows 4*(lane/16)+r
   const int e = eb * 16 + row;
 #pragma unroll
-  for (int b = 0; b < TB; ++b) {
+  for (int r = 0; r < 4; ++r) {
+    const int t = t0 + (lane >> 4) * 4 + r;
+    float v = 0.f;
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int t = t0 + b * 16 + (lane >> 4) * 4 + r;
-      float v = 0.f;
+    for (int u = 0; u < U; ++u) v += acc[u][r];
+    if (t < T) part[(static_cast<size_t>(s) * T + t) * E + e] = v;
+  }
+}
+
+// Large batches: a workgroup takes 64 tokens x kLE experts over one K slice.
+// Each 32-element K step stages the token tile (64 rows) and the three router
+// parts (3 x kLE rows) in LDS with coalesced 16-byte loads, one step of
+// register prefetch and double-buffered LDS; wave w multiplies all 64 tokens
+// against experts 32w .. 32w + 31 out of LDS.  (Loading MFMA fragments
+// straight from global memory touches 16 rows per instruction, which runs at
+// a fraction of the coalesced rate.)
+constexpr int kLE = 128;                // experts per workgroup
+constexpr int kLRow = 80;               // LDS row stride: 64 data bytes + 16 pad
+constexpr int kLRows = 64 + 3 * kLE;    // token rows + router rows per buffer
+constexpr int kLChunks = kLRows * 4;    // 16-byte chunks per step
+constexpr int kLPer = (kLChunks + 255) / 256;
+
+__global__ __launch_bounds__(256) void router_logits_lds_kernel(const uint16_t* __restrict__ x,
+                                                                const uint16_t* __restrict__ wp,
+                                                                int T, int H, int E, int S,
+                                                                float* __restrict__ part) {
+  __shared__ __attribute__((aligned(16))) uint8_t lds[2][kLRows * kLRow];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int t0 = blockIdx.x * 64;
+  const int s = blockIdx.y;
+  const int e0 = blockIdx.z * kLE;
+  const int kbeg = s * (H / S);
+  const int n_steps = (H / S) / 32;
+  const size_t n = static_cast<size_t>(E) * H;
+
+  // this thread's chunks: row r (token rows first, then lo / mid / hi router
+  // rows of the workgroup's experts), 16-byte piece q of the row's 64 bytes
+  const uint16_t* src[kLPer];
+  int dst[kLPer];
 #pragma unroll
-      for (int u = 0; u < U; ++u) v += acc[b][u][r];
-      if (t < T) part[(static_cast<size_t>(s) * T + t) * E + e] = v;
+  for (int i = 0; i < kLPer; ++i) {
+    const int c = min(tid + i * 256, kLChunks - 1);
+    const int r = c >> 2, q = c & 3;
+    if (r < 64) {
+      src[i] = x + static_cast<size_t>(min(t0 + r, T - 1)) * H + kbeg + q * 8;
+    } else {
+      const int rr = r - 64, p = rr / kLE;
+      const int e = min(e0 + rr % kLE, E - 1);
+      // part order in LDS: lo, mid, hi (the accumulation order below)
+      src[i] = wp + static_cast<size_t>(2 - p) * n + static_cast<size_t>(e) * H + kbeg + q * 8;
     }
+    dst[i] = r * kLRow + q * 16;
+  }
+  u32x4 reg[kLPer];
+  auto load = [&](int step) {
+    const int k = min(step, n_steps - 1) * 32;
+#pragma unroll
+    for (int i = 0; i < kLPer; ++i) reg[i] = *reinterpret_cast<const u32x4*>(src[i] + k);
+  };
+  auto store = [&](int buf) {
+#pragma unroll
+    for (int i = 0; i < kLPer; ++i) *reinterpret_cast<u32x4*>(&lds[buf][dst[i]]) = reg[i];
+  };
+
+  f32x4 acc[4][2];
+#pragma unroll
+  for (int b = 0; b < 4; ++b)
+#pragma unroll
+    for (int j = 0; j < 2; ++j) acc[b][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+  const int row = lane & 15;
+  const int kq = (lane >> 4) * 16;  // byte offset of this lane's 8 K values
+  auto compute = [&](int buf) {
+    const uint8_t* L = lds[buf];
+    bf16x8 a[4];
+#pragma unroll
+    for (int b = 0; b < 4; ++b)
+      a[b] = *reinterpret_cast<const bf16x8*>(L + (b * 16 + row) * kLRow + kq);
+#pragma unroll
+    for (int p = 0; p < 3; ++p) {
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const bf16x8 w = *reinterpret_cast<const bf16x8*>(
+            L + (64 + p * kLE + wave * 32 + j * 16 + row) * kLRow + kq);
+#pragma unroll
+        for (int b = 0; b < 4; ++b)
+          acc[b][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[b], w, acc[b][j], 0, 0, 0);
+      }
+    }
+  };
+
+  load(0);
+  store(0);
+  load(1);
+  __syncthreads();
+  for (int step = 0; step < n_steps; ++step) {
+    compute(step & 1);
+    store((step + 1) & 1);
+    load(step + 2);
+    __syncthreads();
+  }
+
+  // 16x16 f32 result: lane holds column (expert) lane%16, rows 4*(lane/16)+r
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const int e = e0 + wave * 32 + j * 16 + row;
+#pragma unroll
+    for (int b = 0; b < 4; ++b)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int t = t0 + b * 16 + (lane >> 4) * 4 + r;
+        if (t < T && e < E) part[(static_cast<size_t>(s) * T + t) * E + e] = acc[b][j][r];
+      }
   }
 }
 
@@ -239,11 +330,11 @@ hipError_t launch_router(const uint16_t* x, const uint16_t* w_packed, const floa
   const int S = router_k_slices(T, H);
   if (T <= 256) {
     const dim3 grid((T + kTokPerWg - 1) / kTokPerWg, E / 16, S);
-    hipLaunchKernelGGL(router_logits_kernel<1>, grid, dim3(256), 0, stream, x, w_packed, T, H, E,
-                       S, part);
+    hipLaunchKernelGGL(router_logits_kernel, grid, dim3(256), 0, stream, x, w_packed, T, H, E, S,
+                       part);
   } else {
-    const dim3 grid((T + kTokPerWg - 1) / kTokPerWg, (E / 16 + kWavesPerWg - 1) / kWavesPerWg, S);
-    hipLaunchKernelGGL(router_logits_kernel<4>, grid, dim3(256), 0, stream, x, w_packed, T, H, E,
+    const dim3 grid((T + 63) / 64, S, (E + kLE - 1) / kLE);
+    hipLaunchKernelGGL(router_logits_lds_kernel, grid, dim3(256), 0, stream, x, w_packed, T, H, E,
                        S, part);
   }
   hipLaunchKernelGGL(router_topk_kernel, dim3((T + kWavesPerWg - 1) / kWavesPerWg), dim3(256), 0,

@@ -162,6 +162,13 @@ def test_quantize_validation(lib):
     assert lib.moe_prenorm(4, 63, FAKE, FAKE, None) == moe.EINVAL
     assert lib.moe_prenorm(0, 64, FAKE, FAKE, None) == moe.OK
     assert lib.moe_residual_add(4, 64, None, FAKE, None) == moe.EINVAL
+    rp = lib.moe_residual_prenorm
+    assert rp(4, 64, None, FAKE, FAKE, None) == moe.EINVAL
+    assert rp(4, 64, FAKE, None, FAKE, None) == moe.EINVAL
+    assert rp(4, 64, FAKE, FAKE, None, None) == moe.EINVAL
+    assert rp(4, 64, FAKE, FAKE, FAKE, None) == moe.EINVAL  # out aliases x
+    assert rp(4, 60, FAKE, FAKE, ctypes.c_void_p(FAKE.value + 4096), None) == moe.EINVAL
+    assert rp(0, 64, FAKE, FAKE, ctypes.c_void_p(FAKE.value + 4096), None) == moe.OK
 
 
 def test_binding_fails_loudly_without_library(monkeypatch):

@@ -370,6 +370,17 @@ def test_prenorm_and_residual(full):
     assert np.all(np.abs(got - ref) <= ulp * 1.0001)
     ref_r = om.residual_add(x.float().numpy(), y.cpu().double().numpy())
     assert np.array_equal(xr.float().cpu().numpy(), ref_r)
+    # the fused step between layers: same x update, and the pre-norm of the
+    # new x bit-identical to the separate call
+    xf = xd.clone()
+    pf = moe.residual_prenorm(xf, y)
+    torch.cuda.synchronize()
+    assert torch.equal(xf, xr)
+    assert torch.equal(pf, moe.prenorm(xr))
+    ref_f = om.prenorm(ref_r)
+    got_f = pf.float().cpu().numpy()
+    ulp_f = np.maximum(np.abs(ref_f), 1e-30) * 2.0 ** -7
+    assert np.all(np.abs(got_f - ref_f) <= ulp_f * 1.0001)
 
 
 def test_stacked_small_shape_nvfp4():
