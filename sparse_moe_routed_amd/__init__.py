@@ -93,6 +93,7 @@ _SIGS = {
 }
 
 _lib = None
+ABI_VERSION = 2  # MOE_ABI_VERSION of include/moe.h this binding describes
 
 
 def lib():
@@ -102,6 +103,10 @@ def lib():
         if not os.path.exists(LIB_PATH):
             raise ImportError(f"{LIB_PATH} is missing: run `python -m sparse_moe_routed_amd.build`")
         l = ctypes.CDLL(LIB_PATH)
+        l.moe_abi_version.restype = ctypes.c_int32
+        if l.moe_abi_version() != ABI_VERSION:
+            raise ImportError(f"{LIB_PATH} has ABI version {l.moe_abi_version()}, this binding "
+                              f"expects {ABI_VERSION}: rebuild with `python -m sparse_moe_routed_amd.build`")
         for name, (res, args) in _SIGS.items():
             fn = getattr(l, name)
             fn.restype = res

@@ -42,7 +42,7 @@ def test_exports_every_declared_symbol(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert moe.abi_version() == header_abi_version()
+    assert moe.abi_version() == header_abi_version() == moe.ABI_VERSION
     assert moe.status_str(moe.OK) == "ok"
     for s in (moe.EINVAL, moe.EUNSUPPORTED, moe.EWORKSPACE, moe.EHIP, 99):
         assert moe.status_str(s)
