@@ -869,8 +869,15 @@ struct PrefillTile<kNVFP4, STAGE> {
 constexpr int kDecodeRows = 32;
 constexpr int kDecodeMaxT = 512;
 
+// below this many tokens the up projection touches so few experts that
+// 64-column tiles (twice the workgroups, more loads in flight per CU) stream
+// the weights faster; the down projection (wider N) does not gain
+constexpr int kNarrowUpMaxT = 16;
+
 template <int FMT, int STAGE>
 hipError_t launch_fmt_stage(int T, const GemmArgs& g, hipStream_t stream) {
+  if (STAGE == 0 && T < kNarrowUpMaxT)
+    return launch_one<FMT, STAGE, kDecodeRows, 64, 1, 2>(g, stream);
   if (T < kDecodeMaxT) return launch_one<FMT, STAGE, kDecodeRows, 128, 1, 4>(g, stream);
   using P = PrefillTile<FMT, STAGE>;
   return launch_dma<FMT, STAGE, P::BM, P::BN, P::WM, P::WN, P::NBUF>(g, stream);
