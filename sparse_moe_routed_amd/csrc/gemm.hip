@@ -588,10 +588,13 @@ __global__ __launch_bounds__(WM* WN * 64) void grouped_gemm_dma_kernel(GemmArgs 
     }
   };
 
-  // row blocks dealt to wave rows in turn (as in grouped_gemm_kernel)
+  // row blocks dealt to wave rows in turn (as in grouped_gemm_kernel).  A
+  // wave whose columns all lie past N (ragged last column tile) multiplies
+  // nothing; it still issues its share of the loads and meets the barriers.
   const int live_blocks = (rows_valid + 31) >> 5;
   int ml_raw = (live_blocks - wm + WM - 1) / WM;
   ml_raw = ml_raw < 0 ? 0 : (ml_raw > MB ? MB : ml_raw);
+  if (n0 + wn * WTN >= N) ml_raw = 0;
   const int ml = __builtin_amdgcn_readfirstlane(ml_raw);
   bool n_live[NB];
 #pragma unroll

@@ -24,25 +24,35 @@ namespace {
 constexpr int kPermThreads = 256;
 constexpr int kRounds = kChunk / kPermThreads;  // entries per thread per chunk
 
-// per-expert counts of one chunk of flat ids into LDS cnt[] (zeroed by the caller)
-__device__ void count_chunk(const int32_t* __restrict__ ids, int R, int E, int chunk,
-                            int32_t* cnt) {
+// this thread's entries of one chunk (round r holds flat index chunk * kChunk
+// + r * kPermThreads + threadIdx.x), all loads issued together: the expert id
+// when it lies in [0, E), else -1 (also past R)
+__device__ __forceinline__ void load_chunk(const int32_t* __restrict__ ids, int R, int E,
+                                           int chunk, int (&ev)[kRounds]) {
   const int base = chunk * kChunk;
+#pragma unroll
   for (int r = 0; r < kRounds; ++r) {
     const int i = base + r * kPermThreads + threadIdx.x;
-    if (i < R) {
-      const int e = ids[i];
-      if (e >= 0 && e < E) atomicAdd(&cnt[e], 1);
-    }
+    const int e = i < R ? ids[i] : -1;
+    ev[r] = (e >= 0 && e < E) ? e : -1;
   }
+}
+
+// per-expert counts of one chunk into LDS cnt[] (zeroed by the caller)
+__device__ __forceinline__ void count_chunk(const int (&ev)[kRounds], int32_t* cnt) {
+#pragma unroll
+  for (int r = 0; r < kRounds; ++r)
+    if (ev[r] >= 0) atomicAdd(&cnt[ev[r]], 1);
 }
 
 __global__ __launch_bounds__(kPermThreads) void perm_count_kernel(
     const int32_t* __restrict__ ids, int R, int E, int32_t* __restrict__ chunk_counts) {
   __shared__ int32_t cnt[256];
+  int ev[kRounds];
+  load_chunk(ids, R, E, blockIdx.x, ev);
   for (int e = threadIdx.x; e < E; e += kPermThreads) cnt[e] = 0;
   __syncthreads();
-  count_chunk(ids, R, E, blockIdx.x, cnt);
+  count_chunk(ev, cnt);
   __syncthreads();
   for (int e = threadIdx.x; e < E; e += kPermThreads)
     chunk_counts[static_cast<size_t>(blockIdx.x) * E + e] = cnt[e];
@@ -114,25 +124,28 @@ __global__ __launch_bounds__(kPermThreads) void perm_scan_kernel(
   scan_experts(run, E, counts, offsets, bm0, tile_off0, bm1, tile_off1, zero_words, n_zero, tmp);
 }
 
-// stable scatter of one chunk; run[e] (LDS) holds the first sorted row of
-// expert e for this chunk and advances past it
-__device__ void scatter_chunk(const int32_t* __restrict__ ids, const float* __restrict__ gates,
-                              int R, int E, int chunk, int32_t* run, int32_t (*wcnt)[256],
+// stable scatter of one chunk (entries from load_chunk); run[e] (LDS) holds
+// the first sorted row of expert e for this chunk and advances past it.
+// Rounds wholly past R are skipped (the test is uniform over the workgroup).
+__device__ void scatter_chunk(const int (&ev)[kRounds], const float* __restrict__ gates, int R,
+                              int E, int chunk, int32_t* run, int32_t (*wcnt)[256],
                               int32_t* __restrict__ sorted_src, int32_t* __restrict__ inv,
                               float* __restrict__ row_gate) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int base = chunk * kChunk;
   const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+  float gv[kRounds];
+#pragma unroll
   for (int r = 0; r < kRounds; ++r) {
     const int i = base + r * kPermThreads + threadIdx.x;
-    int e = -1;
-    if (i < R) {
-      e = ids[i];
-      if (e < 0 || e >= E) {
-        e = -1;
-        inv[i] = -1;
-      }
-    }
+    gv[r] = ev[r] >= 0 ? gates[i] : 0.f;
+  }
+#pragma unroll
+  for (int r = 0; r < kRounds; ++r) {
+    if (base + r * kPermThreads >= R) break;
+    const int i = base + r * kPermThreads + threadIdx.x;
+    const int e = ev[r];
+    if (i < R && e < 0) inv[i] = -1;
     // lanes of this wave holding the same expert
     uint64_t same = __ballot(e >= 0);
 #pragma unroll
@@ -148,7 +161,7 @@ __device__ void scatter_chunk(const int32_t* __restrict__ ids, const float* __re
       for (int w = 0; w < wave; ++w) pos += wcnt[w][e];
       sorted_src[pos] = i;
       inv[i] = pos;
-      row_gate[pos] = gates[i];
+      row_gate[pos] = gv[r];
     }
     __syncthreads();
     for (int ee = threadIdx.x; ee < E; ee += kPermThreads) {
@@ -170,13 +183,15 @@ __global__ __launch_bounds__(kPermThreads) void perm_scatter_kernel(
     float* __restrict__ row_gate) {
   __shared__ int32_t run[256];
   __shared__ int32_t wcnt[kPermThreads / 64][256];
+  int ev[kRounds];
+  load_chunk(ids, R, E, blockIdx.x, ev);
   for (int e = threadIdx.x; e < E; e += kPermThreads) {
     run[e] = offsets[e] + chunk_base[static_cast<size_t>(blockIdx.x) * E + e];
   }
   for (int i = threadIdx.x; i < (kPermThreads / 64) * 256; i += kPermThreads)
     (&wcnt[0][0])[i] = 0;
   __syncthreads();
-  scatter_chunk(ids, gates, R, E, blockIdx.x, run, wcnt, sorted_src, inv, row_gate);
+  scatter_chunk(ev, gates, R, E, blockIdx.x, run, wcnt, sorted_src, inv, row_gate);
 }
 
 // All three steps in one workgroup when the flat ids fit one chunk (decode
@@ -190,11 +205,13 @@ __global__ __launch_bounds__(kPermThreads) void perm_single_kernel(
   __shared__ int32_t cnt[256];
   __shared__ int32_t wcnt[kPermThreads / 64][256];
   __shared__ int tmp[kPermThreads / 64];
+  int ev[kRounds];
+  load_chunk(ids, R, E, 0, ev);
   for (int e = threadIdx.x; e < 256; e += kPermThreads) cnt[e] = 0;
   for (int i = threadIdx.x; i < (kPermThreads / 64) * 256; i += kPermThreads)
     (&wcnt[0][0])[i] = 0;
   __syncthreads();
-  count_chunk(ids, R, E, 0, cnt);
+  count_chunk(ev, cnt);
   __syncthreads();
   const int e = threadIdx.x;
   const int run = e < E ? cnt[e] : 0;
@@ -203,7 +220,7 @@ __global__ __launch_bounds__(kPermThreads) void perm_single_kernel(
   // cnt[] becomes the running first row of each expert
   if (e < E) cnt[e] = offsets[e];
   __syncthreads();
-  scatter_chunk(ids, gates, R, E, 0, cnt, wcnt, sorted_src, inv, row_gate);
+  scatter_chunk(ev, gates, R, E, 0, cnt, wcnt, sorted_src, inv, row_gate);
 }
 
 }  // namespace

@@ -15,9 +15,10 @@
 // router_logits_kernel (T <= 256) and router_logits_lds_kernel (larger
 // batches) write partial logits of S slices of K to the workspace as [S, T, E]
 // fp32; more slices spread small batches over more CUs.
-// router_topk_kernel: one wave per token sums the S partials in order, adds
-// the bias and takes k rounds of wave-wide maximum (DPP reductions, ties to
-// the lower index), then writes the renormalised softmax gates.
+// router_topk_kernel: one wave per token sums the S partials in order (all S
+// loads issued together), adds the bias and takes k rounds of wave-wide
+// maximum (DPP reductions, ties to the lower index), then writes the
+// renormalised softmax gates.
 #include "moe_common.h"
 #include "moe_internal.h"
 
@@ -29,6 +30,7 @@ constexpr int kTokPerWave = 16;
 constexpr int kWavesPerWg = 4;
 constexpr int kTokPerWg = kTokPerWave * kWavesPerWg;
 constexpr int kMaxE = 256;
+constexpr int kMaxSlices = 12;  // router_k_slices never returns more
 
 __global__ __launch_bounds__(256) void router_pack_kernel(const float* __restrict__ w, size_t n,
                                                           uint16_t* __restrict__ packed) {
@@ -234,6 +236,10 @@ __device__ __forceinline__ uint32_t float_key(float f) {
 // takes the largest key over the wave, then the lowest expert index holding
 // it (ballots over the slots in index order), and retires that expert.
 // Gates: z_j = exp(l_j - l_0), summed in slot order, g_j = z_j / sum.
+// MAXS >= S bounds the unrolled slice loads; slices past S read slice S - 1
+// again and add +0 (the running sum starts at +0, so the result is the same
+// as summing exactly S terms).
+template <int MAXS>
 __global__ __launch_bounds__(256) void router_topk_kernel(const float* __restrict__ part,
                                                           const float* __restrict__ bias, int T,
                                                           int E, int S, int k,
@@ -250,9 +256,15 @@ __global__ __launch_bounds__(256) void router_topk_kernel(const float* __restric
     v[i] = -INFINITY;
     key[i] = 0u;
     if (e < E) {
+      float p[MAXS];
+#pragma unroll
+      for (int s = 0; s < MAXS; ++s)
+        p[s] = part[(static_cast<size_t>(min(s, S - 1)) * T + t) * E + e];
+      const float b = bias ? bias[e] : 0.f;
       float l = 0.f;
-      for (int s = 0; s < S; ++s) l += part[(static_cast<size_t>(s) * T + t) * E + e];
-      v[i] = l + (bias ? bias[e] : 0.f);
+#pragma unroll
+      for (int s = 0; s < MAXS; ++s) l += s < S ? p[s] : 0.f;
+      v[i] = l + b;
       key[i] = float_key(v[i]);
     }
   }
@@ -310,7 +322,7 @@ __global__ __launch_bounds__(256) void router_topk_kernel(const float* __restric
 // batches (few token blocks to spread over the CUs), up to 4 otherwise.
 int router_k_slices(int T, int H) {
   const int steps = H / 32;
-  int S = T <= 256 ? 12 : 4;
+  int S = T <= 256 ? kMaxSlices : 4;
   while (S > 1 && steps % S) --S;
   return S;
 }
@@ -337,8 +349,13 @@ hipError_t launch_router(const uint16_t* x, const uint16_t* w_packed, const floa
     hipLaunchKernelGGL(router_logits_lds_kernel, grid, dim3(256), 0, stream, x, w_packed, T, H, E,
                        S, part);
   }
-  hipLaunchKernelGGL(router_topk_kernel, dim3((T + kWavesPerWg - 1) / kWavesPerWg), dim3(256), 0,
-                     stream, part, bias, T, E, S, k, ids, gates);
+  const dim3 tgrid((T + kWavesPerWg - 1) / kWavesPerWg);
+  if (S <= 4)
+    hipLaunchKernelGGL(router_topk_kernel<4>, tgrid, dim3(256), 0, stream, part, bias, T, E, S, k,
+                       ids, gates);
+  else
+    hipLaunchKernelGGL(router_topk_kernel<kMaxSlices>, tgrid, dim3(256), 0, stream, part, bias, T,
+                       E, S, k, ids, gates);
   return hipGetLastError();
 }
 
