@@ -42,7 +42,7 @@
 extern "C" {
 #endif
 
-#define MOE_ABI_VERSION 2
+#define MOE_ABI_VERSION 3
 
 typedef enum {
   MOE_OK = 0,
@@ -81,10 +81,20 @@ typedef struct {
  *   BF16 : up  bf16 [E, F, H],  down bf16 [E, H, F]
  *   FP8  : up  u8 E4M3 [E, F, H], down u8 [E, H, F]; up_s/down_s fp32 [E]
  *          (weight = dec(code) * s)
- *   NVFP4: up  u8 [E, F, H/2],  down u8 [E, H, F/2]  (two E2M1 codes per byte,
- *          element 2i in the low nibble); up_bs u8 E4M3 [E, F, H/16],
- *          down_bs [E, H, F/16]; up_s/down_s fp32 [E]
- *          (weight = dec(code) * dec(block scale) * s)
+ *   NVFP4: up  u8 F*H/2 bytes per expert, down u8 H*F/2 (two E2M1 codes per
+ *          byte, element 2i in the low nibble); up_bs u8 E4M3 F*H/16 bytes
+ *          per expert, down_bs H*F/16 (one per 16-element block along K);
+ *          up_s/down_s fp32 [E]  (weight = dec(code) * dec(block scale) * s).
+ *          Panel layout: a projection's N x K matrix is cut into panels of
+ *          128 rows (the last may be shorter, rows_p = min(128, N - 128 p))
+ *          and each panel is stored K-step-major in steps of 64 elements.
+ *          Code byte j (0..31) of row n, step s lies at
+ *            128 p * K/2 + s * rows_p * 32 + (n - 128 p) * 32 + j,
+ *          block scale j (0..3) of row n, step s at
+ *            128 p * K/16 + s * rows_p * 4 + (n - 128 p) * 4 + j,
+ *          p = n / 128, from the expert's base.  moe_quantize_experts
+ *          writes this layout; a GEMM tile then reads one contiguous block
+ *          per K step.
  * Unused pointers may be NULL. */
 typedef struct {
   int32_t fmt; /* moe_wfmt */
@@ -199,8 +209,8 @@ int32_t moe_quantize_experts(const moe_dims* dims, int32_t fmt,
 /* Per-tensor activation quantiser of moe_forward as a standalone call (same
  * recipes as moe_quantize_experts, amax over the whole [rows, cols] tensor).
  *   x [dev] bf16 [rows, cols]; codes [dev] u8 [rows, cols] (FP8) or
- *   [rows, cols/2] (NVFP4, packed like the weights); bs [dev] u8
- *   [rows, cols/16] (NVFP4 only); scale [dev] fp32 [1] out;
+ *   [rows, cols/2] (NVFP4: two codes per byte as in the weights, row-major);
+ *   bs [dev] u8 [rows, cols/16] (NVFP4 only, row-major); scale [dev] fp32 [1] out;
  *   ws [dev] >= 256 bytes of scratch. */
 int32_t moe_quantize_activation(int32_t fmt, int32_t rows, int32_t cols,
                                 const void* x, void* codes, uint8_t* bs,

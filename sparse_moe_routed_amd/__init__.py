@@ -93,7 +93,7 @@ _SIGS = {
 }
 
 _lib = None
-ABI_VERSION = 2  # MOE_ABI_VERSION of include/moe.h this binding describes
+ABI_VERSION = 3  # MOE_ABI_VERSION of include/moe.h this binding describes
 
 
 def lib():
@@ -309,10 +309,11 @@ def quantize_experts(up: torch.Tensor, down: torch.Tensor, fmt: str,
         down_q = torch.empty((E, H, F), dtype=torch.uint8, device=dev)
         up_bs = down_bs = None
     elif fmt == "nvfp4":
-        up_q = torch.empty((E, F, H // 2), dtype=torch.uint8, device=dev)
-        down_q = torch.empty((E, H, F // 2), dtype=torch.uint8, device=dev)
-        up_bs = torch.empty((E, F, H // 16), dtype=torch.uint8, device=dev)
-        down_bs = torch.empty((E, H, F // 16), dtype=torch.uint8, device=dev)
+        # per-expert byte arrays in the panel layout of moe_experts (moe.h)
+        up_q = torch.empty((E, F * H // 2), dtype=torch.uint8, device=dev)
+        down_q = torch.empty((E, H * F // 2), dtype=torch.uint8, device=dev)
+        up_bs = torch.empty((E, F * H // 16), dtype=torch.uint8, device=dev)
+        down_bs = torch.empty((E, H * F // 16), dtype=torch.uint8, device=dev)
     else:
         raise ValueError(fmt)
     up_s = torch.empty(E, dtype=torch.float32, device=dev)

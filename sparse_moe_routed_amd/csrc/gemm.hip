@@ -53,6 +53,31 @@ constexpr int kStepBytes = 128;  // K bytes of each A/B row staged per step
 constexpr int kPrefetch = 2;     // K steps of loads in flight per thread
 constexpr int kLds = 144;        // padded LDS row stride in bytes
 
+// The expert that owns logical tile `logical`: the largest e in [0, E) with
+// tile_off[e] * n_ntiles <= logical (tile_off is nondecreasing from
+// tile_off[0] = 0, so that set of e is a prefix and its size less one is the
+// answer).  Each lane tests up to four entries (E <= 256), all loaded in one
+// round, and ballots count the entries at or below: one memory round trip
+// before the tile's first loads instead of a dependent binary search.
+__device__ __forceinline__ int owner_expert(const int32_t* __restrict__ tile_off, int E,
+                                            int n_ntiles, int logical) {
+  const int lane = threadIdx.x & 63;
+  int v[4];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const int ee = 1 + lane + 64 * q;
+    v[q] = ee < E ? tile_off[ee] : 0;
+  }
+  int cnt = 0;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const int ee = 1 + lane + 64 * q;
+    cnt += __popcll(__ballot(ee < E && v[q] * n_ntiles <= logical));
+  }
+  return __builtin_amdgcn_readfirstlane(cnt);
+}
+
+
 template <int FMT, int STAGE, int BM, int BN, int WM, int WN>
 __global__ __launch_bounds__(WM* WN * 64) void grouped_gemm_kernel(GemmArgs g) {
   constexpr int NT = WM * WN * 64;
@@ -85,12 +110,7 @@ __global__ __launch_bounds__(WM* WN * 64) void grouped_gemm_kernel(GemmArgs g) {
   if (local >= per_xcd) return;
   const int logical = (blockIdx.x & 7) * per_xcd + local;
   if (logical >= total) return;
-  int lo = 0, hi = g.E;  // largest e with tile_off[e] * n_ntiles <= logical
-  while (hi - lo > 1) {
-    const int mid = (lo + hi) >> 1;
-    if (g.tile_off[mid] * n_ntiles <= logical) lo = mid; else hi = mid;
-  }
-  const int e = lo;
+  const int e = owner_expert(g.tile_off, g.E, n_ntiles, logical);
   const int te = g.tile_off[e + 1] - g.tile_off[e];
   const int loc = logical - g.tile_off[e] * n_ntiles;
   const int ntile = loc / te;
@@ -123,6 +143,10 @@ __global__ __launch_bounds__(WM* WN * 64) void grouped_gemm_kernel(GemmArgs g) {
     a_col[i] = cc * 16;
     a_dst[i] = r * kLds + cc * 16;
   }
+  // NVFP4 panel of this tile and the bytes of one K step of its rows
+  static_assert(FMT != kNVFP4 || kNvPanel % BN == 0, "NVFP4 tiles stay inside one panel");
+  const int nv_pn0 = n0 - n0 % kNvPanel;
+  const int nv_rows = nv_panel_rows(N, nv_pn0 / kNvPanel);
   const uint8_t* b_src[B_CH];
   const uint8_t* s_src[B_CH];
   int b_dst[B_CH], b_col[B_CH];
@@ -130,11 +154,12 @@ __global__ __launch_bounds__(WM* WN * 64) void grouped_gemm_kernel(GemmArgs g) {
   for (int i = 0; i < B_CH; ++i) {
     const int c = (tid + i * NT) % B_TOT;
     if constexpr (FMT == kNVFP4) {
+      // the tile lies inside one panel; per K step its rows are contiguous
       const int r = c >> 1, half = c & 1;
       const int n = min(n0 + r, N - 1);
-      const size_t row = static_cast<size_t>(e) * N + n;
-      b_src[i] = static_cast<const uint8_t*>(g.b) + row * (K / 2) + half * 16;
-      s_src[i] = g.b_bs + row * (K / 16) + half * 2;
+      const size_t pbase = static_cast<size_t>(e) * N + nv_pn0;
+      b_src[i] = static_cast<const uint8_t*>(g.b) + pbase * (K / 2) + (n - nv_pn0) * 32 + half * 16;
+      s_src[i] = g.b_bs + pbase * (K / 16) + (n - nv_pn0) * 4 + half * 2;
       b_dst[i] = r * kLds + half * 64;
       b_col[i] = 0;
     } else if constexpr (FMT == kFP8X) {
@@ -183,8 +208,8 @@ __global__ __launch_bounds__(WM* WN * 64) void grouped_gemm_kernel(GemmArgs g) {
 #pragma unroll
     for (int i = 0; i < B_CH; ++i) {
       if constexpr (FMT == kNVFP4) {
-        b_reg[SET][i] = *reinterpret_cast<const u32x4*>(b_src[i] + step * 32);
-        s_reg[SET][i] = *reinterpret_cast<const uint16_t*>(s_src[i] + step * 4);
+        b_reg[SET][i] = *reinterpret_cast<const u32x4*>(b_src[i] + step * (nv_rows * 32));
+        s_reg[SET][i] = *reinterpret_cast<const uint16_t*>(s_src[i] + step * (nv_rows * 4));
       } else if constexpr (FMT == kFP8X) {
         b_reg[SET][i] = *reinterpret_cast<const u32x4*>(b_src[i] + step * 64);
       } else if constexpr (FMT == kFP8) {
@@ -490,12 +515,7 @@ __global__ __launch_bounds__(WM* WN * 64) void grouped_gemm_dma_kernel(GemmArgs 
   if (local >= per_xcd) return;
   const int logical = (blockIdx.x & 7) * per_xcd + local;
   if (logical >= total) return;
-  int lo = 0, hi = g.E;
-  while (hi - lo > 1) {
-    const int mid = (lo + hi) >> 1;
-    if (g.tile_off[mid] * n_ntiles <= logical) lo = mid; else hi = mid;
-  }
-  const int e = lo;
+  const int e = owner_expert(g.tile_off, g.E, n_ntiles, logical);
   const int te = g.tile_off[e + 1] - g.tile_off[e];
   const int loc = logical - g.tile_off[e] * n_ntiles;
   const int ntile = loc / te;
@@ -533,6 +553,12 @@ __global__ __launch_bounds__(WM* WN * 64) void grouped_gemm_dma_kernel(GemmArgs 
     a_cof[q] = c * 16;
   }
   constexpr int CPR = RB / 16;  // 16-byte chunks per weight row and step
+  // NVFP4 weights sit in panels stored K-step-major (the tile lies inside one
+  // panel): a step of the tile's rows is contiguous, w_step bytes apart
+  static_assert(FMT != kNVFP4 || kNvPanel % BN == 0, "NVFP4 tiles stay inside one panel");
+  const int nv_pn0 = n0 - n0 % kNvPanel;
+  const int nv_rows = nv_panel_rows(N, nv_pn0 / kNvPanel);
+  const int w_step = (FMT == kNVFP4) ? nv_rows * RB : RB;
   const uint8_t* b_src[QB];
   int b_dst[QB], b_cof[QB];
 #pragma unroll
@@ -541,7 +567,12 @@ __global__ __launch_bounds__(WM* WN * 64) void grouped_gemm_dma_kernel(GemmArgs 
     const int r = qi * (1024 / RB) + lane / CPR;
     const int c = (lane % CPR) ^ lds_swz<RB>(r);
     const int n = min(n0 + r, N - 1);
-    b_src[q] = static_cast<const uint8_t*>(g.b) + (static_cast<size_t>(e) * N + n) * w_bytes + c * 16;
+    if constexpr (FMT == kNVFP4) {
+      b_src[q] = static_cast<const uint8_t*>(g.b) + (static_cast<size_t>(e) * N + nv_pn0) * w_bytes +
+                 (n - nv_pn0) * RB + c * 16;
+    } else {
+      b_src[q] = static_cast<const uint8_t*>(g.b) + (static_cast<size_t>(e) * N + n) * w_bytes + c * 16;
+    }
     b_dst[q] = B_OFF + qi * 1024;
     b_cof[q] = c * 16;
   }
@@ -552,7 +583,7 @@ __global__ __launch_bounds__(WM* WN * 64) void grouped_gemm_dma_kernel(GemmArgs 
     for (int q = 0; q < QS; ++q) {
       const int qi = (wave + q * NW) % NSC;
       const int n = min(n0 + qi * 64 + lane, N - 1);
-      s_src[q] = g.b_bs + (static_cast<size_t>(e) * N + n) * (K / 16);
+      s_src[q] = g.b_bs + (static_cast<size_t>(e) * N + nv_pn0) * (K / 16) + (n - nv_pn0) * 4;
       s_dst[q] = S_OFF + qi * 256;
     }
   }
@@ -571,7 +602,7 @@ __global__ __launch_bounds__(WM* WN * 64) void grouped_gemm_dma_kernel(GemmArgs 
       __builtin_amdgcn_global_load_lds(p, (__attribute__((address_space(3))) void*)(buf + a_dst[q]),
                                        16, 0, 0);
     }
-    const int wb = step * RB;                  // weight bytes before this step
+    const int wb = step * w_step;              // weight bytes before this step
 #pragma unroll
     for (int q = 0; q < QB; ++q) {
       const uint8_t* p = b_src[q] + wb;
@@ -582,7 +613,7 @@ __global__ __launch_bounds__(WM* WN * 64) void grouped_gemm_dma_kernel(GemmArgs 
     if constexpr (QS > 0) {
 #pragma unroll
       for (int q = 0; q < QS; ++q)
-        __builtin_amdgcn_global_load_lds(s_src[q] + step * 4,
+        __builtin_amdgcn_global_load_lds(s_src[q] + step * (nv_rows * 4),
                                          (__attribute__((address_space(3))) void*)(buf + s_dst[q]),
                                          4, 0, 0);
     }

@@ -13,6 +13,21 @@ constexpr int kFP8X = 3;
 
 constexpr int kChunk = 2048;  // flat (token, slot) entries per permutation chunk
 
+// NVFP4 expert banks: each expert projection [N, K] is cut into panels of
+// kNvPanel rows (the last one may be shorter), and each panel is stored
+// K-step-major: for step s (64 elements of K) the panel's rows follow one
+// another, 32 code bytes each in the code array and 4 block-scale bytes each
+// in the scale array.  Panel p starts where row-major row p * kNvPanel would,
+// so the arrays keep their row-major sizes.  A GEMM tile of at most kNvPanel
+// columns inside one panel then reads one contiguous block per K step.
+constexpr int kNvPanel = 128;
+constexpr int kNvStepK = 64;
+
+__host__ __device__ __forceinline__ int nv_panel_rows(int N, int p) {
+  const int left = N - p * kNvPanel;
+  return left < kNvPanel ? left : kNvPanel;
+}
+
 struct PermBufs {
   int32_t* chunk_counts;  // [n_chunks, E]
   int32_t* chunk_base;    // [n_chunks, E]
@@ -50,8 +65,9 @@ struct GemmArgs {
   const int32_t* sorted_src;  // up only: flat index of each sorted row
   int top_k;
   const void* a;              // up: tokens [T, K]; down: activations [R, K]
-  const void* b;              // expert weights, [E, N, K] (packed K/2 for nvfp4)
-  const uint8_t* b_bs;        // nvfp4 block scales [E, N, K/16]
+  const void* b;              // expert weights, [E, N, K] (nvfp4: N*K/2 bytes per expert
+                              // in kNvPanel-row panels, K-step-major)
+  const uint8_t* b_bs;        // nvfp4 block scales, N*K/16 bytes per expert, same panels
   const float* b_s;           // fp8 / nvfp4 weight scale per expert [E]
   const float* a_s;           // fp8 / nvfp4 activation scale (device scalar)
   int N, K;

@@ -178,8 +178,9 @@ __global__ __launch_bounds__(kQThreads) void weight_amax_kernel(const uint16_t* 
 }
 
 __global__ __launch_bounds__(kQThreads) void weight_codes_kernel(
-    int fmt, const uint16_t* __restrict__ w, size_t per_expert, const uint32_t* amax,
+    int fmt, const uint16_t* __restrict__ w, int N, int K, const uint32_t* amax,
     uint8_t* __restrict__ q, uint8_t* __restrict__ bs) {
+  const size_t per_expert = static_cast<size_t>(N) * K;
   const int e = blockIdx.y;
   const float a = __uint_as_float(amax[e]);
   const uint16_t* base = w + static_cast<size_t>(e) * per_expert;
@@ -243,8 +244,20 @@ __global__ __launch_bounds__(kQThreads) void weight_codes_kernel(
                 << (8 * j);
         }
       }
-      reinterpret_cast<uint2*>(qe)[i] = make_uint2(p0, p1);
-      be[i] = static_cast<uint8_t>(sb);
+      // block i = row n, block b of the row; stored in the panel layout (rows
+      // of a panel contiguous per 64-element K step: 32 code bytes, 4 scales)
+      const size_t n = i / static_cast<size_t>(K / 16);
+      const int b = static_cast<int>(i - n * static_cast<size_t>(K / 16));
+      const int p = static_cast<int>(n / kNvPanel), pr = static_cast<int>(n % kNvPanel);
+      const int rows_p = nv_panel_rows(N, p);
+      const int st = b / (kNvStepK / 16), bq = b % (kNvStepK / 16);
+      const size_t pn0 = static_cast<size_t>(p) * kNvPanel;
+      const size_t code_at = pn0 * (K / 2) + static_cast<size_t>(st) * rows_p * (kNvStepK / 2) +
+                             static_cast<size_t>(pr) * (kNvStepK / 2) + bq * 8;
+      const size_t scale_at = pn0 * (K / 16) + static_cast<size_t>(st) * rows_p * (kNvStepK / 16) +
+                              static_cast<size_t>(pr) * (kNvStepK / 16) + bq;
+      *reinterpret_cast<uint2*>(qe + code_at) = make_uint2(p0, p1);
+      be[scale_at] = static_cast<uint8_t>(sb);
     }
   }
 }
@@ -306,7 +319,7 @@ hipError_t launch_quant_weights(int fmt, const uint16_t* w, int E, int N, int K,
   hipLaunchKernelGGL(weight_amax_kernel, dim3(gx, E), dim3(kQThreads), 0, stream, w, per,
                      reinterpret_cast<uint32_t*>(s));
   const int gq = grid_for(per / 16, 64);
-  hipLaunchKernelGGL(weight_codes_kernel, dim3(gq, E), dim3(kQThreads), 0, stream, fmt, w, per,
+  hipLaunchKernelGGL(weight_codes_kernel, dim3(gq, E), dim3(kQThreads), 0, stream, fmt, w, N, K,
                      reinterpret_cast<const uint32_t*>(s), q, bs);
   hipLaunchKernelGGL(weight_scales_kernel, dim3((E + 255) / 256), dim3(256), 0, stream, fmt, E,
                      s);

@@ -122,6 +122,9 @@ WORKLOADS = {
     "decode_t64_bf16": dict(T=64, fmt="bf16", outliers=False, layers=1),
     "prefill_t4096_bf16": dict(T=4096, fmt="bf16", outliers=True, layers=1),
     "decode_t64_fp8": dict(T=64, fmt="fp8", outliers=False, layers=1),
+    "decode_t4_fp8": dict(T=4, fmt="fp8", outliers=False, layers=1),
+    "decode_t64_nvfp4": dict(T=64, fmt="nvfp4", outliers=False, layers=1),
+    "decode_t4_nvfp4": dict(T=4, fmt="nvfp4", outliers=False, layers=1),
     "prefill_t4096_fp8": dict(T=4096, fmt="fp8", outliers=False, layers=1),
     "prefill_t4096_nvfp4": dict(T=4096, fmt="nvfp4", outliers=False, layers=1),
     "stack23_t4096_nvfp4": dict(T=4096, fmt="nvfp4", outliers=False, layers=N_MOE_LAYERS),

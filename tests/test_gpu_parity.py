@@ -319,12 +319,26 @@ def test_forward_large_batch_sampled(full):
 
 
 # --------------------------------------------------------------------------- quantisers
+def _panels_to_rows(buf: np.ndarray, N: int, K: int, row_step_bytes: int) -> np.ndarray:
+    """Row-major [N, K/64 * row_step_bytes] view of one expert's NVFP4 bytes in
+    the panel layout of moe_experts: 128-row panels, each K-step-major with
+    row_step_bytes per row and 64-element step (32 for codes, 4 for scales)."""
+    S = K // 64
+    out = np.empty((N, S * row_step_bytes), np.uint8)
+    for p0 in range(0, N, 128):
+        rows = min(128, N - p0)
+        blk = buf[p0 * S * row_step_bytes:(p0 + rows) * S * row_step_bytes]
+        out[p0:p0 + rows] = blk.reshape(S, rows, row_step_bytes).transpose(1, 0, 2).reshape(rows, -1)
+    return out
+
+
 @pytest.mark.parametrize("fmt", ["fp8", "nvfp4"])
 def test_weight_codes_bit_exact(full, fmt):
     bank = full.bank(fmt)
     torch.cuda.synchronize()
+    H, F = FULL.hidden, FULL.ffn
     for e in (0, 77, 127):
-        for name, w in (("up", full.up[e]), ("down", full.down[e])):
+        for name, w, (N, K) in (("up", full.up[e], (F, H)), ("down", full.down[e], (H, F))):
             wf = w.float().numpy()
             q_gpu = getattr(bank, name)[e].cpu().numpy()
             s_gpu = getattr(bank, name + "_s")[e].item()
@@ -333,8 +347,9 @@ def test_weight_codes_bit_exact(full, fmt):
                 assert np.array_equal(q_gpu, q), (name, e)
             else:
                 q, sb, s = codecs.nvfp4_quantize(wf)
-                assert np.array_equal(q_gpu, codecs.nvfp4_pack(q)), (name, e)
-                assert np.array_equal(getattr(bank, name + "_bs")[e].cpu().numpy(), sb), (name, e)
+                assert np.array_equal(_panels_to_rows(q_gpu, N, K, 32), codecs.nvfp4_pack(q)), (name, e)
+                sb_gpu = getattr(bank, name + "_bs")[e].cpu().numpy()
+                assert np.array_equal(_panels_to_rows(sb_gpu, N, K, 4), sb), (name, e)
             assert np.float32(s_gpu) == np.float32(s), (name, e)
 
 
