@@ -8,15 +8,16 @@
 //
 // A workgroup computes a BM x BN tile of one expert: BM sorted rows of that
 // expert (row tiles counted by the permutation on the device) times BN output
-// columns.  Both operands are K-contiguous.  Two kernels, one per regime:
-//   grouped_gemm_kernel (decode batches, 32-row tiles): weight streaming; each
-//     thread loads 16-byte chunks two K steps ahead into registers and stores
-//     them into double-buffered LDS (rows padded to 144 bytes); weight codes
-//     of the expanded formats are converted on the way into LDS.
-//   grouped_gemm_dma_kernel (prefill, 128-row tiles): operands go from global
-//     memory straight into LDS (global_load_lds_dwordx4) as stored, into an
-//     XOR-swizzled layout; weight codes are expanded per lane when the MFMA
-//     fragments are formed.  See the comment above that kernel.
+// columns.  Both operands are K-contiguous.  Two kernels:
+//   grouped_gemm_kernel (BF16 and FP8 decode batches, 32-row tiles): weight
+//     streaming; each thread loads 16-byte chunks two K steps ahead into
+//     registers and stores them into double-buffered LDS (rows padded to 144
+//     bytes); FP8 up-projection codes are expanded on the way into LDS.
+//   grouped_gemm_dma_kernel (prefill, 128-row tiles, and NVFP4 decode,
+//     32-row tiles): operands go from global memory straight into LDS
+//     (global_load_lds_dwordx4) as stored, into an XOR-swizzled layout; weight
+//     codes are expanded per lane when the MFMA fragments are formed.  See
+//     the comment above that kernel.
 // Formats:
 //   BF16 : v_mfma_f32_32x32x16_bf16, 64 K per step.
 //   FP8  : v_mfma_scale_f32_32x32x64_f8f6f4 with unit E8M0 scales (E4M3 x
@@ -37,7 +38,9 @@
 //          [2^-10, 2688], so every fp16 value is exact; activations arrive as
 //          the same exact fp16 products.  Then v_mfma_f32_32x32x16_f16 (exact
 //          products, fp32 sums); the two fp32 tensor scales are applied in the
-//          epilogue.
+//          epilogue.  Codes and block scales are read in the bank's panel
+//          layout (128-row panels, K-step-major), one contiguous block per
+//          K step of a tile.
 // Epilogues: up writes bf16(relu(h)^2) (and the tensor amax for quantised
 // formats); down writes fp32 gate * h per sorted row.
 #include <type_traits>
@@ -83,12 +86,15 @@ __global__ __launch_bounds__(WM* WN * 64) void grouped_gemm_kernel(GemmArgs g) {
   constexpr int NT = WM * WN * 64;
   constexpr int WTM = BM / WM, WTN = BN / WN;  // wave tile
   constexpr int MB = WTM / 32, NB = WTN / 32;  // 32x32 MFMA blocks per wave
-  // 16-byte source chunks per step: A rows 8 each; B rows 8 (bf16 / fp8),
-  // 4 (fp8 expanded: 64 codes) or 2 (nvfp4: 64 codes packed).  When a tile has
-  // fewer chunks than threads, the extra threads repeat a chunk (same data to
-  // the same LDS bytes), which keeps the loads branch-free.
+  // NVFP4 tiles of every size run in grouped_gemm_dma_kernel, which keeps the
+  // codes packed in LDS.
+  static_assert(FMT != kNVFP4, "NVFP4 uses the direct-load kernel");
+  // 16-byte source chunks per step: A rows 8 each; B rows 8 (bf16 / fp8) or
+  // 4 (fp8 expanded: 64 codes).  When a tile has fewer chunks than threads,
+  // the extra threads repeat a chunk (same data to the same LDS bytes), which
+  // keeps the loads branch-free.
   constexpr int A_TOT = BM * 8;
-  constexpr int B_TOT = (FMT == kNVFP4) ? BN * 2 : (FMT == kFP8X ? BN * 4 : BN * 8);
+  constexpr int B_TOT = (FMT == kFP8X) ? BN * 4 : BN * 8;
   constexpr int A_CH = (A_TOT + NT - 1) / NT;
   constexpr int B_CH = (B_TOT + NT - 1) / NT;
   constexpr int ESZ = (FMT == kFP8) ? 1 : 2;   // bytes per staged element
@@ -143,31 +149,16 @@ __global__ __launch_bounds__(WM* WN * 64) void grouped_gemm_kernel(GemmArgs g) {
     a_col[i] = cc * 16;
     a_dst[i] = r * kLds + cc * 16;
   }
-  // NVFP4 panel of this tile and the bytes of one K step of its rows
-  static_assert(FMT != kNVFP4 || kNvPanel % BN == 0, "NVFP4 tiles stay inside one panel");
-  const int nv_pn0 = n0 - n0 % kNvPanel;
-  const int nv_rows = nv_panel_rows(N, nv_pn0 / kNvPanel);
   const uint8_t* b_src[B_CH];
-  const uint8_t* s_src[B_CH];
   int b_dst[B_CH], b_col[B_CH];
 #pragma unroll
   for (int i = 0; i < B_CH; ++i) {
     const int c = (tid + i * NT) % B_TOT;
-    if constexpr (FMT == kNVFP4) {
-      // the tile lies inside one panel; per K step its rows are contiguous
-      const int r = c >> 1, half = c & 1;
-      const int n = min(n0 + r, N - 1);
-      const size_t pbase = static_cast<size_t>(e) * N + nv_pn0;
-      b_src[i] = static_cast<const uint8_t*>(g.b) + pbase * (K / 2) + (n - nv_pn0) * 32 + half * 16;
-      s_src[i] = g.b_bs + pbase * (K / 16) + (n - nv_pn0) * 4 + half * 2;
-      b_dst[i] = r * kLds + half * 64;
-      b_col[i] = 0;
-    } else if constexpr (FMT == kFP8X) {
+    if constexpr (FMT == kFP8X) {
       const int r = c >> 2, q = c & 3;  // 16 codes of the row's 64 per step
       const int n = min(n0 + r, N - 1);
       const size_t row = static_cast<size_t>(e) * N + n;
       b_src[i] = static_cast<const uint8_t*>(g.b) + row * K + q * 16;
-      s_src[i] = nullptr;
       b_dst[i] = r * kLds + q * 32;
       b_col[i] = 0;
     } else {
@@ -175,7 +166,6 @@ __global__ __launch_bounds__(WM* WN * 64) void grouped_gemm_kernel(GemmArgs g) {
       const int n = min(n0 + r, N - 1);
       const size_t row = static_cast<size_t>(e) * N + n;
       b_src[i] = static_cast<const uint8_t*>(g.b) + row * k_bytes + cc * 16;
-      s_src[i] = nullptr;
       b_dst[i] = r * kLds + cc * 16;
       b_col[i] = cc * 16;
     }
@@ -185,7 +175,6 @@ __global__ __launch_bounds__(WM* WN * 64) void grouped_gemm_kernel(GemmArgs g) {
   // step s is multiplied out of LDS
   u32x4 a_reg[kPrefetch][A_CH];
   u32x4 b_reg[kPrefetch][B_CH];
-  uint32_t s_reg[kPrefetch][B_CH];
 
   // Loads are issued unconditionally (no branches around vector memory ops,
   // so the compiler can wait for exactly the set it needs): steps past the end
@@ -207,10 +196,7 @@ __global__ __launch_bounds__(WM* WN * 64) void grouped_gemm_kernel(GemmArgs g) {
     }
 #pragma unroll
     for (int i = 0; i < B_CH; ++i) {
-      if constexpr (FMT == kNVFP4) {
-        b_reg[SET][i] = *reinterpret_cast<const u32x4*>(b_src[i] + step * (nv_rows * 32));
-        s_reg[SET][i] = *reinterpret_cast<const uint16_t*>(s_src[i] + step * (nv_rows * 4));
-      } else if constexpr (FMT == kFP8X) {
+      if constexpr (FMT == kFP8X) {
         b_reg[SET][i] = *reinterpret_cast<const u32x4*>(b_src[i] + step * 64);
       } else if constexpr (FMT == kFP8) {
         const bool tail = kb + b_col[i] >= k_bytes;
@@ -230,31 +216,7 @@ __global__ __launch_bounds__(WM* WN * 64) void grouped_gemm_kernel(GemmArgs g) {
     for (int i = 0; i < A_CH; ++i) *reinterpret_cast<u32x4*>(A + a_dst[i]) = a_reg[SET][i];
 #pragma unroll
     for (int i = 0; i < B_CH; ++i) {
-      if constexpr (FMT == kNVFP4) {
-        // 32 E2M1 codes (element 2j in the low nibble of byte j), two block scales
-        const _Float16 sc0 = static_cast<_Float16>(e4m3_decode(s_reg[SET][i] & 0xffu));
-        const _Float16 sc1 = static_cast<_Float16>(e4m3_decode((s_reg[SET][i] >> 8) & 0xffu));
-        uint32_t outw[16];
-#pragma unroll
-        for (int w = 0; w < 4; ++w) {
-          const uint32_t word = b_reg[SET][i][w];
-          const _Float16 sc = w < 2 ? sc0 : sc1;
-          const f16x2 s2 = {sc, sc};
-          // two E2M1 values per byte as fp16 (unit scale), times the block scale
-          const f16x2 p0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(word, 1.0f, 0) * s2;
-          const f16x2 p1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(word, 1.0f, 1) * s2;
-          const f16x2 p2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(word, 1.0f, 2) * s2;
-          const f16x2 p3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(word, 1.0f, 3) * s2;
-          outw[w * 4 + 0] = __builtin_bit_cast(uint32_t, p0);
-          outw[w * 4 + 1] = __builtin_bit_cast(uint32_t, p1);
-          outw[w * 4 + 2] = __builtin_bit_cast(uint32_t, p2);
-          outw[w * 4 + 3] = __builtin_bit_cast(uint32_t, p3);
-        }
-        u32x4* dst = reinterpret_cast<u32x4*>(B + b_dst[i]);
-#pragma unroll
-        for (int q = 0; q < 4; ++q)
-          dst[q] = u32x4{outw[4 * q], outw[4 * q + 1], outw[4 * q + 2], outw[4 * q + 3]};
-      } else if constexpr (FMT == kFP8X) {
+      if constexpr (FMT == kFP8X) {
         // 16 E4M3 codes -> 16 bf16 (unit scale: exact)
         uint32_t outw[8];
 #pragma unroll
@@ -335,7 +297,7 @@ __global__ __launch_bounds__(WM* WN * 64) void grouped_gemm_kernel(GemmArgs g) {
                   af[i], bfr[j], acc[i][j], 0, 0, 0, 127, 0, 127);
         }
       } else {
-        using frag = std::conditional_t<FMT == kNVFP4, f16x8, bf16x8>;
+        using frag = bf16x8;
         // fragments of sub-step s+1 are read while the MFMAs of sub-step s run
         frag af[2][ML], bfr[2][NB];
         auto rd = [&](int s, int slot) {
@@ -355,14 +317,9 @@ __global__ __launch_bounds__(WM* WN * 64) void grouped_gemm_kernel(GemmArgs g) {
 #pragma unroll
           for (int i = 0; i < ML; ++i)
 #pragma unroll
-            for (int j = 0; j < NB; ++j) {
-              if constexpr (FMT == kNVFP4)
-                acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af[s & 1][i], bfr[s & 1][j],
-                                                                   acc[i][j], 0, 0, 0);
-              else
-                acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[s & 1][i], bfr[s & 1][j],
-                                                                    acc[i][j], 0, 0, 0);
-            }
+            for (int j = 0; j < NB; ++j)
+              acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[s & 1][i], bfr[s & 1][j],
+                                                                  acc[i][j], 0, 0, 0);
         }
       }
     }
@@ -899,9 +856,12 @@ struct PrefillTile<kNVFP4, STAGE> {
   static constexpr int BM = 128, BN = 128, WM = 2, WN = 2, NBUF = 2;
 };
 
-// decode batches: 32-row tiles in the register-staged kernel
+// decode batches: 32-row tiles, in the register-staged kernel (BF16, FP8) or
+// the direct-load kernel with three LDS buffers (NVFP4: packed codes in LDS
+// take a quarter of the expanded fp16 bytes, measured fastest)
 constexpr int kDecodeRows = 32;
 constexpr int kDecodeMaxT = 512;
+constexpr int kNvDecodeBuffers = 3;
 
 // below this many tokens the up projection touches so few experts that
 // 64-column tiles (twice the workgroups, more loads in flight per CU) stream
@@ -910,9 +870,14 @@ constexpr int kNarrowUpMaxT = 16;
 
 template <int FMT, int STAGE>
 hipError_t launch_fmt_stage(int T, const GemmArgs& g, hipStream_t stream) {
-  if (STAGE == 0 && T < kNarrowUpMaxT)
-    return launch_one<FMT, STAGE, kDecodeRows, 64, 1, 2>(g, stream);
-  if (T < kDecodeMaxT) return launch_one<FMT, STAGE, kDecodeRows, 128, 1, 4>(g, stream);
+  if constexpr (FMT == kNVFP4) {
+    if (T < kDecodeMaxT)
+      return launch_dma<FMT, STAGE, kDecodeRows, 128, 1, 4, kNvDecodeBuffers>(g, stream);
+  } else {
+    if (STAGE == 0 && T < kNarrowUpMaxT)
+      return launch_one<FMT, STAGE, kDecodeRows, 64, 1, 2>(g, stream);
+    if (T < kDecodeMaxT) return launch_one<FMT, STAGE, kDecodeRows, 128, 1, 4>(g, stream);
+  }
   using P = PrefillTile<FMT, STAGE>;
   return launch_dma<FMT, STAGE, P::BM, P::BN, P::WM, P::WN, P::NBUF>(g, stream);
 }
