@@ -18,7 +18,8 @@
  *     tensors); [host] are host pointers read during the call only.
  *   - All device work is enqueued asynchronously on `stream` (a hipStream_t;
  *     NULL = the null stream).  No call synchronises with the host.
- *   - Row-major, contiguous layouts; bf16 is passed as raw 16-bit words.
+ *   - Row-major, contiguous layouts, except the packed NVFP4 expert bank
+ *     (128-row panels, see moe_experts); bf16 is passed as raw 16-bit words.
  *   - The caller owns every buffer.  The library allocates no device memory;
  *     scratch comes from the caller's workspace (moe_workspace_size).
  *   - Arguments are validated on the host before any launch.  On error the

@@ -284,6 +284,7 @@ def forward_timed(x: torch.Tensor, ids: torch.Tensor, gates: torch.Tensor, exper
     _dev(x, torch.bfloat16, "x", (T, dims.hidden))
     _dev(ids, torch.int32, "ids", (T, dims.top_k))
     _dev(gates, torch.float32, "gates", (T, dims.top_k))
+    _dev(ws, torch.uint8, "ws")
     _dev(y, y_dtype, "y", (T, dims.hidden))
     yd = {torch.float32: Y_F32, torch.bfloat16: Y_BF16}[y_dtype]
     arr = (ctypes.c_void_p * len(events))(*[ctypes.c_void_p(e) for e in events])
