@@ -43,6 +43,9 @@ def parse():
     p.add_argument("--warmup", type=int, default=5)
     p.add_argument("--workload", default="decode_t64_bf16")
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--graph", action="store_true",
+                   help="also capture one step into a HIP graph and time K replays "
+                        "(reported beside the eager headline)")
     p.add_argument("--copy-calibration", action="store_true",
                    help="only run a plain 1 GiB device copy (reference for HBM byte counters)")
     return p.parse_args()
@@ -207,6 +210,32 @@ def main():
         for h in er + es:
             hip.destroy(h)
 
+    # pass 3 (optional): the same step captured once into a HIP graph (the
+    # library's calls hold no host sync, allocation or memset), K replays
+    # between two synchronisations
+    graph_rec = None
+    if args.graph:
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            step()
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            step()
+        for _ in range(args.warmup):
+            graph.replay()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(args.steps):
+            graph.replay()
+        torch.cuda.synchronize()
+        gwall = time.perf_counter() - t0
+        graph_rec = {"ms_per_step": round(gwall * 1e3 / args.steps, 4),
+                     "value": round(T * args.steps / gwall, 1), "steps": args.steps}
+        del graph
+
     # ---------------------------------------------------------------- roofline
     ids_h = ids.cpu().numpy()
     touched = int(np.unique(ids_h).size)
@@ -266,6 +295,8 @@ def main():
         "stage_ms": {k2: round(v, 4) for k2, v in stage_ms.items()},
         "roofline": roof,
     }
+    if graph_rec:
+        out["graph"] = graph_rec
 
     # ---------------------------------------------------------------- CPU oracle
     if not args.no_cpu_baseline:

@@ -424,3 +424,51 @@ def test_stacked_small_shape_nvfp4():
     err, _ = _rel_err(xg.float().cpu().numpy()[keep], xo[keep])
     _log(f"stacked {n_layers} layers: max|d|/rms = {err:.3e}, diverged tokens {int(diverged.sum())}")
     assert err <= TOL["nvfp4"]
+
+
+# --------------------------------------------------------------------------- graph capture
+@pytest.mark.parametrize("fmt", ["bf16", "nvfp4"])
+def test_route_forward_in_hip_graph(full, fmt):
+    # route + forward captured into one HIP graph (no host sync, no allocation
+    # and no memset nodes on the path: scratch is cleared by kernels) and
+    # replayed on three inputs.  Eager work runs between replays, and every
+    # replay must equal the eager result on the same input bit for bit.
+    T, ld = 64, _ld(FULL)
+    bank = full.bank(fmt)
+    x0 = _x(T, FULL).cuda()
+    inputs = [x0, x0.flip(0).contiguous(), (x0.float() * 0.5).to(torch.bfloat16)]
+    x = torch.empty_like(x0)
+    ids = torch.empty((T, FULL.top_k), dtype=torch.int32, device="cuda")
+    gates = torch.empty((T, FULL.top_k), dtype=torch.float32, device="cuda")
+    y = torch.empty((T, FULL.hidden), dtype=torch.float32, device="cuda")
+    ws = moe.workspace(ld, fmt, T)
+    rws = moe.route_workspace(ld, T)
+
+    def step():
+        moe.route(x, full.router, ld, ids=ids, gates=gates, ws=rws)
+        moe.forward(x, ids, gates, bank, ld, ws=ws, y=y)
+
+    x.copy_(inputs[0])
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        step()
+    torch.cuda.synchronize()
+    for i, inp in enumerate(inputs * 2):
+        x.copy_(inp)
+        step()
+        torch.cuda.synchronize()
+        ids_ref, y_ref = ids.clone(), y.clone()
+        ids.fill_(-7)
+        y.fill_(float("nan"))
+        x.copy_(inp)
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(ids, ids_ref), (fmt, i)
+        assert torch.equal(y, y_ref), (fmt, i)
+    _log(f"{fmt}: {len(inputs) * 2} graph replays equal to eager")
