@@ -111,6 +111,17 @@ def make_tokens(T: int, dims: Dims = Dims(), outliers: bool = False) -> torch.Te
     return _to_bf16(x)
 
 
+def make_tokens_device(T: int, dims: Dims = Dims(), seed: int = 6000,
+                       device: str = "cuda") -> torch.Tensor:
+    """bf16 activations x [T, H] drawn on the device (torch generator seeded
+    with `seed`): for batches too large to generate on the host.  Callers that
+    need host copies of some rows copy them back."""
+    g = torch.Generator(device=device)
+    g.manual_seed(seed)
+    x = torch.randn((T, dims.hidden), generator=g, device=device, dtype=torch.float32)
+    return x.to(torch.bfloat16)
+
+
 def make_f32(shape, seed: int) -> torch.Tensor:
     """Standard-normal fp32 tensor from rng(seed) (generic test rows)."""
     return torch.from_numpy(np.random.default_rng(seed).standard_normal(shape, dtype=np.float32))

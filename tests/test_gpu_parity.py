@@ -318,6 +318,37 @@ def test_forward_large_batch_sampled(full):
     assert err <= TOL["bf16"]
 
 
+def test_forward_max_tokens_sampled(full):
+    # the largest batch the ABI accepts (2^20 tokens, 6.3M routed rows): x is
+    # drawn on the device; the oracle checks a sample of tokens
+    T, E, R = 1 << 20, FULL.n_experts, (1 << 20) * FULL.top_k
+    xd = synth.make_tokens_device(T, FULL)
+    ids_g, g_g = moe.route(xd, full.router)
+    ws = moe.workspace(_ld(FULL), "bf16", T)
+    y = moe.forward(xd, ids_g, g_g, full.bank("bf16"), ws=ws)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(2)
+    sample = np.unique(np.concatenate([rng.choice(T, 16, replace=False), [0, T - 1]]))
+    idx = torch.from_numpy(sample).cuda()
+    xs = xd[idx].float().cpu().numpy()
+    ids_o, g_o, gap, _ = om.route(xs, full.w_r.numpy(), full.b.numpy(), FULL.top_k)
+    ig = ids_g[idx].cpu().numpy()
+    same = np.array([sorted(a) == sorted(b) for a, b in zip(ig, ids_o)])
+    assert np.all(same | (gap < om.NEAR_TIE))
+    y_ref = om.forward(xs, ids_o, g_o, full.oracle_bank("bf16").preload(np.unique(ids_o), 16))
+    err, _ = _rel_err(y[idx].double().cpu().numpy()[same], y_ref[same])
+    _log(f"T={T} sample of {len(sample)}: max|d|/rms = {err:.3e}")
+    assert err <= TOL["bf16"]
+    # the device histogram and prefix sum against a count of the ids
+    lay = moe.workspace_layout(_ld(FULL), "bf16", T)
+    counts = torch.bincount(ids_g.flatten().long(), minlength=E).cpu().numpy()
+    assert np.array_equal(_ws_int32(ws, lay["counts"], E), counts)
+    offsets = _ws_int32(ws, lay["offsets"], E + 1)
+    assert offsets[0] == 0 and offsets[-1] == R and np.array_equal(np.diff(offsets), counts)
+    del xd, y, ids_g, g_g, ws
+    torch.cuda.empty_cache()
+
+
 # --------------------------------------------------------------------------- quantisers
 def _panels_to_rows(buf: np.ndarray, N: int, K: int, row_step_bytes: int) -> np.ndarray:
     """Row-major [N, K/64 * row_step_bytes] view of one expert's NVFP4 bytes in
