@@ -364,9 +364,11 @@ __global__ __launch_bounds__(WM* WN * 64) void grouped_gemm_kernel(GemmArgs g) {
 
   // ---- epilogue.  32x32 f32 result: lane holds column lane%32 and rows
   // 8*(r/4) + 4*(lane/32) + r%4 for r = 0..15.
-  // scales of the quantised formats: s_act * s_weight, exact in double
+  // scales of the quantised formats: s_act * s_weight, exact in double; the
+  // up projection takes it rounded once to fp32
   double scale = 1.0;
   if constexpr (FMT != kBF16) scale = static_cast<double>(g.a_s[0]) * static_cast<double>(g.b_s[e]);
+  const float scale_f = static_cast<float>(scale);
   float local_max = 0.f;
 #pragma unroll
   for (int i = 0; i < MB; ++i) {
@@ -381,10 +383,11 @@ __global__ __launch_bounds__(WM* WN * 64) void grouped_gemm_kernel(GemmArgs g) {
         if (rl < rows_valid && col < N) {
           const size_t at = static_cast<size_t>(row0 + rl) * N + col;
           if constexpr (STAGE == 0) {
-            // a = bf16(relu(h)^2): h^2 is exact in double, so a is rounded once
-            double h = static_cast<double>(acc[i][j][r]);
-            if constexpr (FMT != kBF16) h *= scale;
-            const uint16_t b = h > 0.0 ? f64_to_bf16(h * h) : static_cast<uint16_t>(0);
+            // a = bf16(relu(h)^2), rounded once from the exact square of the
+            // fp32 h (BF16: the accumulator itself)
+            float h = acc[i][j][r];
+            if constexpr (FMT != kBF16) h *= scale_f;
+            const uint16_t b = relu_sq_bf16(h);
             static_cast<uint16_t*>(g.out)[at] = b;
             if constexpr (FMT != kBF16) local_max = fmaxf(local_max, bf16_to_f32(b));
           } else {
@@ -776,6 +779,7 @@ __global__ __launch_bounds__(WM* WN * 64) void grouped_gemm_dma_kernel(GemmArgs 
   // ---- epilogue (as in grouped_gemm_kernel)
   double scale = 1.0;
   if constexpr (FMT != kBF16) scale = static_cast<double>(g.a_s[0]) * static_cast<double>(g.b_s[e]);
+  const float scale_f = static_cast<float>(scale);
   float local_max = 0.f;
 #pragma unroll
   for (int i = 0; i < MB; ++i) {
@@ -790,10 +794,11 @@ __global__ __launch_bounds__(WM* WN * 64) void grouped_gemm_dma_kernel(GemmArgs 
         if (rl < rows_valid && col < N) {
           const size_t at = static_cast<size_t>(row0 + rl) * N + col;
           if constexpr (STAGE == 0) {
-            // a = bf16(relu(h)^2): h^2 is exact in double, so a is rounded once
-            double h = static_cast<double>(acc[i][j][r]);
-            if constexpr (FMT != kBF16) h *= scale;
-            const uint16_t b = h > 0.0 ? f64_to_bf16(h * h) : static_cast<uint16_t>(0);
+            // a = bf16(relu(h)^2), rounded once from the exact square of the
+            // fp32 h (BF16: the accumulator itself)
+            float h = acc[i][j][r];
+            if constexpr (FMT != kBF16) h *= scale_f;
+            const uint16_t b = relu_sq_bf16(h);
             static_cast<uint16_t*>(g.out)[at] = b;
             if constexpr (FMT != kBF16) local_max = fmaxf(local_max, bf16_to_f32(b));
           } else {

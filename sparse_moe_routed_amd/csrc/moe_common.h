@@ -47,6 +47,25 @@ __device__ __forceinline__ uint16_t f64_to_bf16(double d) {
   return static_cast<uint16_t>(sign | bits);
 }
 
+// bf16(relu(h)^2), rounded once (nearest, ties to even) from the exact
+// square: h*h = hi + lo exactly, hi = fp32(h*h) and lo = fma(h, h, -hi).
+// The nearest bf16 of hi + lo is that of hi unless hi lies exactly on a bf16
+// midpoint (low 16 bits 0x8000): every other fp32 value is at least one fp32
+// ulp from the midpoints, farther than |lo| <= ulp(hi) / 2.  On a midpoint
+// the sign of lo breaks the tie; lo == 0 is a true tie (to even).
+__device__ __forceinline__ uint16_t relu_sq_bf16(float h) {
+  if (!(h > 0.f)) return 0;
+  const float hi = h * h;
+  const float lo = __builtin_fmaf(h, h, -hi);
+  uint32_t u = __float_as_uint(hi);
+  if ((u & 0xffffu) == 0x8000u && lo != 0.f) {
+    if (lo > 0.f) u += 0x8000u;  // above the midpoint: up; below: truncate
+  } else {
+    u += 0x7fffu + ((u >> 16) & 1u);
+  }
+  return static_cast<uint16_t>(u >> 16);
+}
+
 // ----------------------------------------------------------------- E4M3 (OCP E4M3FN)
 // 1 sign, 4 exponent bits (bias 7), 3 mantissa bits, largest finite 448,
 // subnormals m * 2^-9.  Encode: nearest-even, finite inputs saturate to 448,
