@@ -201,6 +201,14 @@ def test_forward_max_experts_and_k(wide, fmt, T):
     _forward_case(wide, fmt, T)
 
 
+@pytest.mark.parametrize("fmt", ["bf16", "fp8", "nvfp4"])
+@pytest.mark.parametrize("T", [15, 16, 511])
+def test_forward_tile_regime_boundaries(full, fmt, T):
+    # 15 | 16: 64-column up-projection tiles below 16 tokens, 128-column from
+    # 16; 511: the largest batch on the 32-row decode tiles
+    _forward_case(full, fmt, T, outliers=T > 100)
+
+
 @pytest.mark.parametrize("fmt", ["fp8", "nvfp4"])
 @pytest.mark.parametrize("T", [4, 64])
 def test_forward_quantised_full_shape(full, fmt, T):
