@@ -70,19 +70,27 @@ __device__ __forceinline__ uint16_t relu_sq_bf16(float h) {
 // 1 sign, 4 exponent bits (bias 7), 3 mantissa bits, largest finite 448,
 // subnormals m * 2^-9.  Encode: nearest-even, finite inputs saturate to 448,
 // sign bit set iff v < 0.
+//
+// The encoders use the hardware converts (v_cvt_pk_fp8_f32 here,
+// v_cvt_scalef32_pk_fp4_f32 for E2M1 below, unit scale).  Over all fp32 bit
+// patterns with |v| <= 464 (E4M3) or |v| <= 1e30 (E2M1) they give the codes of
+// a bit-level encoder of the definition, except that they keep the sign of
+// -0.  Clamping to the largest finite value first makes saturation hold for
+// every input, and adding +0 turns -0 into +0.
+__device__ __forceinline__ float e4m3_prep(float v) {
+  return __builtin_amdgcn_fmed3f(v, -448.f, 448.f) + 0.f;
+}
+
+// codes of a, b, c, d in bytes 0, 1, 2, 3
+__device__ __forceinline__ uint32_t e4m3_encode4(float a, float b, float c, float d) {
+  const int lo = __builtin_amdgcn_cvt_pk_fp8_f32(e4m3_prep(a), e4m3_prep(b), 0, false);
+  return static_cast<uint32_t>(
+      __builtin_amdgcn_cvt_pk_fp8_f32(e4m3_prep(c), e4m3_prep(d), lo, true));
+}
+
 __device__ __forceinline__ uint32_t e4m3_encode(float v) {
-  const uint32_t sign = v < 0.f ? 0x80u : 0u;
-  const float a = fminf(fabsf(v), 448.f);
-  if (a < 0.015625f) {  // below the smallest normal 2^-6: quantum 2^-9
-    return sign | static_cast<uint32_t>(rintf(a * 512.f));  // 0..8 (8 == 2^-6)
-  }
-  const uint32_t b = __float_as_uint(a);
-  int e = static_cast<int>(b >> 23) - 127;  // -6..8
-  uint32_t keep = (b >> 20) & 7u;
-  const uint32_t rest = b & 0xfffffu;
-  if (rest > 0x80000u || (rest == 0x80000u && (keep & 1u))) ++keep;
-  if (keep == 8u) { keep = 0u; ++e; }
-  return sign | (static_cast<uint32_t>(e + 7) << 3) | keep;
+  return static_cast<uint32_t>(__builtin_amdgcn_cvt_pk_fp8_f32(e4m3_prep(v), 0.f, 0, false)) &
+         0xffu;
 }
 
 __device__ __forceinline__ float e4m3_decode(uint32_t c) {
@@ -98,17 +106,24 @@ __device__ __forceinline__ float e4m3_decode(uint32_t c) {
 
 // ----------------------------------------------------------------- E2M1 (OCP FP4)
 // 1 sign, 2 exponent bits (bias 1), 1 mantissa bit: {0, .5, 1, 1.5, 2, 3, 4, 6}.
+// Encode: nearest-even, saturating to 6, sign bit set iff v < 0 (hardware
+// convert, see the E4M3 encoders).
+__device__ __forceinline__ float e2m1_prep(float v) {
+  return __builtin_amdgcn_fmed3f(v, -6.f, 6.f) + 0.f;
+}
+
 __device__ __forceinline__ uint32_t e2m1_encode(float v) {
-  const uint32_t sign = v < 0.f ? 8u : 0u;
-  const float a = fminf(fabsf(v), 6.f);
-  if (a < 1.f) return sign | static_cast<uint32_t>(rintf(a * 2.f));  // 0, 1, 2(=1.0)
-  const uint32_t b = __float_as_uint(a);
-  int e = static_cast<int>(b >> 23) - 127;  // 0..2
-  uint32_t keep = (b >> 22) & 1u;
-  const uint32_t rest = b & 0x3fffffu;
-  if (rest > 0x200000u || (rest == 0x200000u && (keep & 1u))) ++keep;
-  if (keep == 2u) { keep = 0u; ++e; }
-  return sign | (static_cast<uint32_t>(e + 1) << 1) | keep;
+  return __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(0u, e2m1_prep(v), 0.f, 1.0f, 0) & 0xfu;
+}
+
+// codes of v[0..7]: element 2i in the low nibble of byte i
+__device__ __forceinline__ uint32_t e2m1_encode8(const float* v) {
+  uint32_t w = 0u;
+  w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, e2m1_prep(v[0]), e2m1_prep(v[1]), 1.0f, 0);
+  w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, e2m1_prep(v[2]), e2m1_prep(v[3]), 1.0f, 1);
+  w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, e2m1_prep(v[4]), e2m1_prep(v[5]), 1.0f, 2);
+  w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, e2m1_prep(v[6]), e2m1_prep(v[7]), 1.0f, 3);
+  return w;
 }
 
 __device__ __forceinline__ float e2m1_decode(uint32_t c) {

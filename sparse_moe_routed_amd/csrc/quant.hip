@@ -44,8 +44,9 @@ __global__ __launch_bounds__(kQThreads) void amax_bf16_kernel(const uint16_t* __
   block_amax_to_slots(m, amax);
 }
 
-// FP8: 16 elements per thread.  mode 0 writes dec(code) as bf16 (exact) into
-// deq; mode 1 writes the codes.
+// FP8: 8 elements (one 16-byte load) per thread step, so a wave moves 1 KB
+// of contiguous input per load.  mode 0 writes dec(code) as bf16 (exact)
+// into deq; mode 1 writes the codes.
 __global__ __launch_bounds__(kQThreads) void quant_fp8_kernel(const uint16_t* __restrict__ x,
                                                               const int32_t* n_rows_dev, int rows,
                                                               int cols, const uint32_t* amax_p,
@@ -55,43 +56,42 @@ __global__ __launch_bounds__(kQThreads) void quant_fp8_kernel(const uint16_t* __
   const float amax = read_amax_slots(amax_p);
   if (blockIdx.x == 0 && threadIdx.x == 0) *scale = amax > 0.f ? __fdiv_rn(amax, 448.f) : 0.f;
   const int nr = n_rows_dev ? min(*n_rows_dev, rows) : rows;
-  const size_t n16 = static_cast<size_t>(nr) * cols / 16;
+  const size_t n8 = static_cast<size_t>(nr) * cols / 8;
+  // amax == 0: inv = 0, every product is +-0 and every code 0
   const float inv = amax > 0.f ? __fdiv_rn(448.f, amax) : 0.f;
-  for (size_t i = static_cast<size_t>(blockIdx.x) * kQThreads + threadIdx.x; i < n16;
+  for (size_t i = static_cast<size_t>(blockIdx.x) * kQThreads + threadIdx.x; i < n8;
        i += static_cast<size_t>(gridDim.x) * kQThreads) {
-    const u32x4 v0 = reinterpret_cast<const u32x4*>(x)[2 * i];
-    const u32x4 v1 = reinterpret_cast<const u32x4*>(x)[2 * i + 1];
-    uint32_t q[16];
+    const u32x4 v = reinterpret_cast<const u32x4*>(x)[i];
+    uint32_t c[2];
 #pragma unroll
-    for (int w = 0; w < 4; ++w) {
-      const uint32_t a = v0[w], b = v1[w];
-      q[2 * w] = amax > 0.f ? e4m3_encode(bf16_to_f32(a & 0xffffu) * inv) : 0u;
-      q[2 * w + 1] = amax > 0.f ? e4m3_encode(bf16_to_f32(a >> 16) * inv) : 0u;
-      q[8 + 2 * w] = amax > 0.f ? e4m3_encode(bf16_to_f32(b & 0xffffu) * inv) : 0u;
-      q[8 + 2 * w + 1] = amax > 0.f ? e4m3_encode(bf16_to_f32(b >> 16) * inv) : 0u;
+    for (int h = 0; h < 2; ++h) {
+      const uint32_t a = v[2 * h], b = v[2 * h + 1];
+      c[h] = e4m3_encode4(__uint_as_float(a << 16) * inv, __uint_as_float(a & 0xffff0000u) * inv,
+                          __uint_as_float(b << 16) * inv, __uint_as_float(b & 0xffff0000u) * inv);
     }
     if (mode == 0) {
-      uint32_t o[8];
-#pragma unroll
-      for (int j = 0; j < 8; ++j)
-        o[j] = (__float_as_uint(e4m3_decode(q[2 * j])) >> 16) |
-               (__float_as_uint(e4m3_decode(q[2 * j + 1])) & 0xffff0000u);
-      reinterpret_cast<u32x4*>(deq)[2 * i] = u32x4{o[0], o[1], o[2], o[3]};
-      reinterpret_cast<u32x4*>(deq)[2 * i + 1] = u32x4{o[4], o[5], o[6], o[7]};
+      // every E4M3 value is a bf16 value: the hardware expansion is exact
+      const bf16x2 d0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(c[0], 1.0f, false);
+      const bf16x2 d1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(c[0], 1.0f, true);
+      const bf16x2 d2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(c[1], 1.0f, false);
+      const bf16x2 d3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(c[1], 1.0f, true);
+      reinterpret_cast<u32x4*>(deq)[i] =
+          u32x4{__builtin_bit_cast(uint32_t, d0), __builtin_bit_cast(uint32_t, d1),
+                __builtin_bit_cast(uint32_t, d2), __builtin_bit_cast(uint32_t, d3)};
     } else {
-      uint32_t out[4];
-#pragma unroll
-      for (int w = 0; w < 4; ++w)
-        out[w] = q[4 * w] | (q[4 * w + 1] << 8) | (q[4 * w + 2] << 16) | (q[4 * w + 3] << 24);
-      reinterpret_cast<u32x4*>(codes)[i] = u32x4{out[0], out[1], out[2], out[3]};
+      reinterpret_cast<uint2*>(codes)[i] = make_uint2(c[0], c[1]);
     }
   }
 }
 
-// NVFP4: one 16-element block per thread.  mode 0 writes the fp16 values
-// dec(q) * dec(sb) into deq, which may alias x (at most 6 significant bits and
-// inside [2^-10, 2688]: exact in fp16, the operand type of the NVFP4 GEMM);
-// mode 1 writes packed codes and block scale codes.
+// NVFP4: 8 elements per thread step; the two halves of a 16-element block sit
+// on neighbouring lanes (i even and i + 1), which exchange their amax with
+// one DPP move.  n8 is even (cols is a multiple of 16) and the grid stride is
+// a multiple of 64, so both halves of a block are in the same wave and the
+// same loop iteration.  mode 0 writes the fp16 values dec(q) * dec(sb) into
+// deq, which may alias x (at most 6 significant bits and inside [2^-10,
+// 2688]: exact in fp16, the operand type of the NVFP4 GEMM); mode 1 writes
+// packed codes and block scale codes.
 __global__ __launch_bounds__(kQThreads) void quant_nvfp4_kernel(
     const uint16_t* x, const int32_t* n_rows_dev, int rows, int cols, const uint32_t* amax_p,
     int mode, uint16_t* deq, uint8_t* __restrict__ codes, uint8_t* __restrict__ bs,
@@ -101,57 +101,48 @@ __global__ __launch_bounds__(kQThreads) void quant_nvfp4_kernel(
   if (blockIdx.x == 0 && threadIdx.x == 0 && scale) *scale = S;
   const float sixS = 6.f * S;
   const int nr = n_rows_dev ? min(*n_rows_dev, rows) : rows;
-  const size_t nblk = static_cast<size_t>(nr) * cols / 16;
-  for (size_t i = static_cast<size_t>(blockIdx.x) * kQThreads + threadIdx.x; i < nblk;
+  const size_t n8 = static_cast<size_t>(nr) * cols / 8;
+  for (size_t i = static_cast<size_t>(blockIdx.x) * kQThreads + threadIdx.x; i < n8;
        i += static_cast<size_t>(gridDim.x) * kQThreads) {
-    const u32x4 v0 = reinterpret_cast<const u32x4*>(x)[2 * i];
-    const u32x4 v1 = reinterpret_cast<const u32x4*>(x)[2 * i + 1];
-    float v[16];
+    const u32x4 u = reinterpret_cast<const u32x4*>(x)[i];
+    float v[8];
 #pragma unroll
     for (int w = 0; w < 4; ++w) {
-      v[2 * w] = bf16_to_f32(v0[w] & 0xffffu);
-      v[2 * w + 1] = bf16_to_f32(v0[w] >> 16);
-      v[8 + 2 * w] = bf16_to_f32(v1[w] & 0xffffu);
-      v[8 + 2 * w + 1] = bf16_to_f32(v1[w] >> 16);
+      v[2 * w] = __uint_as_float(u[w] << 16);
+      v[2 * w + 1] = __uint_as_float(u[w] & 0xffff0000u);
     }
-    float amax_b = 0.f;
+    float m = 0.f;
 #pragma unroll
-    for (int j = 0; j < 16; ++j) amax_b = fmaxf(amax_b, fabsf(v[j]));
+    for (int j = 0; j < 8; ++j) m = fmaxf(m, fabsf(v[j]));
+    // quad_perm [1, 0, 3, 2]: the value of the neighbouring lane
+    const float mo = __builtin_bit_cast(
+        float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, m), 0xb1, 0xf, 0xf, false));
+    const float amax_b = fmaxf(m, mo);
     uint32_t sb = 0u;
     float sbf = 0.f;
     if (S > 0.f) {
       sb = e4m3_encode(__fdiv_rn(amax_b, sixS));
       sbf = e4m3_decode(sb);
     }
-    uint32_t q[16];
-    if (sbf > 0.f) {
-      const float r = __fdiv_rn(1.f, sbf * S);
+    // sb == 0: r = 0, every product is +-0 and every code 0
+    const float r = sbf > 0.f ? __fdiv_rn(1.f, sbf * S) : 0.f;
+    float t[8];
 #pragma unroll
-      for (int j = 0; j < 16; ++j) q[j] = e2m1_encode(v[j] * r);
-    } else {
-#pragma unroll
-      for (int j = 0; j < 16; ++j) q[j] = 0u;
-    }
+    for (int j = 0; j < 8; ++j) t[j] = v[j] * r;
+    const uint32_t q = e2m1_encode8(t);
     if (mode == 0) {
-      uint32_t o[8];
-#pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const _Float16 d0 = static_cast<_Float16>(e2m1_decode(q[2 * j]) * sbf);  // exact
-        const _Float16 d1 = static_cast<_Float16>(e2m1_decode(q[2 * j + 1]) * sbf);
-        o[j] = static_cast<uint32_t>(__builtin_bit_cast(uint16_t, d0)) |
-               (static_cast<uint32_t>(__builtin_bit_cast(uint16_t, d1)) << 16);
-      }
-      reinterpret_cast<u32x4*>(deq)[2 * i] = u32x4{o[0], o[1], o[2], o[3]};
-      reinterpret_cast<u32x4*>(deq)[2 * i + 1] = u32x4{o[4], o[5], o[6], o[7]};
+      const _Float16 sh = static_cast<_Float16>(sbf);  // E4M3 values are fp16 values
+      const f16x2 s2 = {sh, sh};
+      const f16x2 p0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(q, 1.0f, 0) * s2;
+      const f16x2 p1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(q, 1.0f, 1) * s2;
+      const f16x2 p2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(q, 1.0f, 2) * s2;
+      const f16x2 p3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(q, 1.0f, 3) * s2;
+      reinterpret_cast<u32x4*>(deq)[i] =
+          u32x4{__builtin_bit_cast(uint32_t, p0), __builtin_bit_cast(uint32_t, p1),
+                __builtin_bit_cast(uint32_t, p2), __builtin_bit_cast(uint32_t, p3)};
     } else {
-      uint32_t p0 = 0u, p1 = 0u;
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        p0 |= (q[2 * j] | (q[2 * j + 1] << 4)) << (8 * j);
-        p1 |= (q[8 + 2 * j] | (q[8 + 2 * j + 1] << 4)) << (8 * j);
-      }
-      reinterpret_cast<uint2*>(codes)[i] = make_uint2(p0, p1);
-      bs[i] = static_cast<uint8_t>(sb);
+      reinterpret_cast<uint32_t*>(codes)[i] = q;
+      if (!(i & 1)) bs[i >> 1] = static_cast<uint8_t>(sb);
     }
   }
 }
@@ -295,7 +286,7 @@ hipError_t launch_amax_bf16(const uint16_t* x, const int32_t* n_rows_dev, int ro
 hipError_t launch_quant_fp8(const uint16_t* x, const int32_t* n_rows_dev, int rows, int cols,
                             const uint32_t* amax, int mode, uint16_t* deq, uint8_t* codes,
                             float* scale, hipStream_t stream) {
-  const int grid = grid_for(static_cast<size_t>(rows) * cols / 16, 4096);
+  const int grid = grid_for(static_cast<size_t>(rows) * cols / 8, 4096);
   hipLaunchKernelGGL(quant_fp8_kernel, dim3(grid), dim3(kQThreads), 0, stream, x, n_rows_dev,
                      rows, cols, amax, mode, deq, codes, scale);
   return hipGetLastError();
@@ -304,7 +295,7 @@ hipError_t launch_quant_fp8(const uint16_t* x, const int32_t* n_rows_dev, int ro
 hipError_t launch_quant_nvfp4(const uint16_t* x, const int32_t* n_rows_dev, int rows, int cols,
                               const uint32_t* amax, int mode, uint16_t* deq, uint8_t* codes,
                               uint8_t* bs, float* scale, hipStream_t stream) {
-  const int grid = grid_for(static_cast<size_t>(rows) * cols / 16, 4096);
+  const int grid = grid_for(static_cast<size_t>(rows) * cols / 8, 4096);
   hipLaunchKernelGGL(quant_nvfp4_kernel, dim3(grid), dim3(kQThreads), 0, stream, x, n_rows_dev,
                      rows, cols, amax, mode, deq, codes, bs, scale);
   return hipGetLastError();
