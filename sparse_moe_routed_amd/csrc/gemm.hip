@@ -868,9 +868,13 @@ constexpr int kDecodeRows = 32;
 constexpr int kDecodeMaxT = 512;
 constexpr int kNvDecodeBuffers = 3;
 
-// below this many tokens the up projection touches so few experts that
-// 64-column tiles (twice the workgroups, more loads in flight per CU) stream
-// the weights faster; the down projection (wider N) does not gain
+// Below this many tokens the up projection touches so few experts that its
+// workgroups cannot be spread evenly over the CUs (about 2.3 per CU at four
+// tokens with 64-column tiles, so a third of the CUs stream 3 while the rest
+// stream 2).  Narrower tiles give more, smaller work units: 32 columns and
+// one wave for BF16, 64 columns and two waves for the expanded FP8 codes
+// (measured fastest at four tokens; the down projection, with its wider N,
+// is fastest with 128 columns).
 constexpr int kNarrowUpMaxT = 16;
 
 template <int FMT, int STAGE>
@@ -879,8 +883,10 @@ hipError_t launch_fmt_stage(int T, const GemmArgs& g, hipStream_t stream) {
     if (T < kDecodeMaxT)
       return launch_dma<FMT, STAGE, kDecodeRows, 128, 1, 4, kNvDecodeBuffers>(g, stream);
   } else {
-    if (STAGE == 0 && T < kNarrowUpMaxT)
+    if (STAGE == 0 && T < kNarrowUpMaxT) {
+      if constexpr (FMT == kBF16) return launch_one<FMT, STAGE, kDecodeRows, 32, 1, 1>(g, stream);
       return launch_one<FMT, STAGE, kDecodeRows, 64, 1, 2>(g, stream);
+    }
     if (T < kDecodeMaxT) return launch_one<FMT, STAGE, kDecodeRows, 128, 1, 4>(g, stream);
   }
   using P = PrefillTile<FMT, STAGE>;
