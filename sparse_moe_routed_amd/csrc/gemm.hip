@@ -9,12 +9,14 @@
 // A workgroup computes a BM x BN tile of one expert: BM sorted rows of that
 // expert (row tiles counted by the permutation on the device) times BN output
 // columns.  Both operands are K-contiguous.  Two kernels:
-//   grouped_gemm_kernel (BF16 and FP8 decode batches, 32-row tiles): weight
-//     streaming; each thread loads 16-byte chunks two K steps ahead into
-//     registers and stores them into double-buffered LDS (rows padded to 144
-//     bytes); FP8 up-projection codes are expanded on the way into LDS.
-//   grouped_gemm_dma_kernel (prefill, 128-row tiles, and NVFP4 decode,
-//     32-row tiles): operands go from global memory straight into LDS
+//   grouped_gemm_kernel (BF16 and FP8 up-projection decode batches, 32-row
+//     tiles): weight streaming; each thread loads 16-byte chunks two K steps
+//     ahead into registers and stores them into double-buffered LDS (rows
+//     padded to 144 bytes); FP8 up-projection codes are expanded on the way
+//     into LDS.
+//   grouped_gemm_dma_kernel (prefill, 128-row tiles, and NVFP4 and FP8
+//     down-projection decode, 32-row tiles): operands go from global memory
+//     straight into LDS
 //     (global_load_lds_dwordx4) as stored, into an XOR-swizzled layout; weight
 //     codes are expanded per lane when the MFMA fragments are formed.  See
 //     the comment above that kernel.
@@ -86,18 +88,18 @@ __global__ __launch_bounds__(WM* WN * 64) void grouped_gemm_kernel(GemmArgs g) {
   constexpr int NT = WM * WN * 64;
   constexpr int WTM = BM / WM, WTN = BN / WN;  // wave tile
   constexpr int MB = WTM / 32, NB = WTN / 32;  // 32x32 MFMA blocks per wave
-  // NVFP4 tiles of every size run in grouped_gemm_dma_kernel, which keeps the
-  // codes packed in LDS.
-  static_assert(FMT != kNVFP4, "NVFP4 uses the direct-load kernel");
-  // 16-byte source chunks per step: A rows 8 each; B rows 8 (bf16 / fp8) or
-  // 4 (fp8 expanded: 64 codes).  When a tile has fewer chunks than threads,
+  // NVFP4 and the FP8 down projection (fp8 MFMA) run in
+  // grouped_gemm_dma_kernel at every size.
+  static_assert(FMT == kBF16 || FMT == kFP8X, "BF16 and expanded FP8 only");
+  // 16-byte source chunks per step: A rows 8 each; B rows 8 (bf16) or 4 (fp8
+  // expanded: 64 codes).  When a tile has fewer chunks than threads,
   // the extra threads repeat a chunk (same data to the same LDS bytes), which
   // keeps the loads branch-free.
   constexpr int A_TOT = BM * 8;
   constexpr int B_TOT = (FMT == kFP8X) ? BN * 4 : BN * 8;
   constexpr int A_CH = (A_TOT + NT - 1) / NT;
   constexpr int B_CH = (B_TOT + NT - 1) / NT;
-  constexpr int ESZ = (FMT == kFP8) ? 1 : 2;   // bytes per staged element
+  constexpr int ESZ = 2;  // bytes per staged element
   static_assert(MB >= 1 && NB >= 1 && A_CH >= 1 && B_CH >= 1, "tile shape");
 
   __shared__ __attribute__((aligned(16))) uint8_t lds[2 * (BM + BN) * kLds];
@@ -133,7 +135,7 @@ __global__ __launch_bounds__(WM* WN * 64) void grouped_gemm_kernel(GemmArgs g) {
 
   // ---- per-thread global sources (fixed over K)
   const uint8_t* a_src[A_CH];
-  int a_dst[A_CH], a_col[A_CH];
+  int a_dst[A_CH];
 #pragma unroll
   for (int i = 0; i < A_CH; ++i) {
     const int c = (tid + i * NT) % A_TOT;
@@ -146,11 +148,10 @@ __global__ __launch_bounds__(WM* WN * 64) void grouped_gemm_kernel(GemmArgs g) {
       src = static_cast<size_t>(row0 + rr);
     }
     a_src[i] = static_cast<const uint8_t*>(g.a) + src * k_bytes + cc * 16;
-    a_col[i] = cc * 16;
     a_dst[i] = r * kLds + cc * 16;
   }
   const uint8_t* b_src[B_CH];
-  int b_dst[B_CH], b_col[B_CH];
+  int b_dst[B_CH];
 #pragma unroll
   for (int i = 0; i < B_CH; ++i) {
     const int c = (tid + i * NT) % B_TOT;
@@ -160,14 +161,12 @@ __global__ __launch_bounds__(WM* WN * 64) void grouped_gemm_kernel(GemmArgs g) {
       const size_t row = static_cast<size_t>(e) * N + n;
       b_src[i] = static_cast<const uint8_t*>(g.b) + row * K + q * 16;
       b_dst[i] = r * kLds + q * 32;
-      b_col[i] = 0;
     } else {
       const int r = c >> 3, cc = c & 7;
       const int n = min(n0 + r, N - 1);
       const size_t row = static_cast<size_t>(e) * N + n;
       b_src[i] = static_cast<const uint8_t*>(g.b) + row * k_bytes + cc * 16;
       b_dst[i] = r * kLds + cc * 16;
-      b_col[i] = cc * 16;
     }
   }
 
@@ -178,30 +177,18 @@ __global__ __launch_bounds__(WM* WN * 64) void grouped_gemm_kernel(GemmArgs g) {
 
   // Loads are issued unconditionally (no branches around vector memory ops,
   // so the compiler can wait for exactly the set it needs): steps past the end
-  // re-read the last step, and the FP8 K tail reads an in-range chunk and
-  // replaces it by zeros.
+  // re-read the last step.  K is a multiple of 64, so bf16 rows hold whole
+  // 128-byte steps.
   auto load = [&](int step_in, auto set_c) {
     constexpr int SET = decltype(set_c)::value;
     const int step = min(step_in, n_steps - 1);
     const int kb = step * kStepBytes;
 #pragma unroll
-    for (int i = 0; i < A_CH; ++i) {
-      if constexpr (FMT == kFP8) {
-        const bool tail = kb + a_col[i] >= k_bytes;
-        const u32x4 v = *reinterpret_cast<const u32x4*>(a_src[i] + (tail ? kb - 64 : kb));
-        a_reg[SET][i] = tail ? u32x4{0u, 0u, 0u, 0u} : v;
-      } else {
-        a_reg[SET][i] = *reinterpret_cast<const u32x4*>(a_src[i] + kb);
-      }
-    }
+    for (int i = 0; i < A_CH; ++i) a_reg[SET][i] = *reinterpret_cast<const u32x4*>(a_src[i] + kb);
 #pragma unroll
     for (int i = 0; i < B_CH; ++i) {
       if constexpr (FMT == kFP8X) {
         b_reg[SET][i] = *reinterpret_cast<const u32x4*>(b_src[i] + step * 64);
-      } else if constexpr (FMT == kFP8) {
-        const bool tail = kb + b_col[i] >= k_bytes;
-        const u32x4 v = *reinterpret_cast<const u32x4*>(b_src[i] + (tail ? kb - 64 : kb));
-        b_reg[SET][i] = tail ? u32x4{0u, 0u, 0u, 0u} : v;
       } else {
         b_reg[SET][i] = *reinterpret_cast<const u32x4*>(b_src[i] + kb);
       }
@@ -269,58 +256,29 @@ __global__ __launch_bounds__(WM* WN * 64) void grouped_gemm_kernel(GemmArgs g) {
     if constexpr (ML > 0) {
       const uint8_t* A = As + buf * BM * kLds;
       const uint8_t* B = Bs + buf * BN * kLds;
-      if constexpr (FMT == kFP8) {
+      using frag = bf16x8;
+      // fragments of sub-step s+1 are read while the MFMAs of sub-step s run
+      frag af[2][ML], bfr[2][NB];
+      auto rd = [&](int s, int slot) {
 #pragma unroll
-        for (int s = 0; s < 2; ++s) {  // 64 K per MFMA
-          i32x8 af[ML], bfr[NB];
+        for (int i = 0; i < ML; ++i)
+          af[slot][i] = *reinterpret_cast<const frag*>(
+              A + ((i * WM + wm) * 32 + lrow) * kLds + s * 32 + lk * 16);
 #pragma unroll
-          for (int i = 0; i < ML; ++i) {
-            const uint8_t* p = A + ((i * WM + wm) * 32 + lrow) * kLds + s * 64 + lk * 32;
-            const u32x4 lo = *reinterpret_cast<const u32x4*>(p);
-            const u32x4 hi = *reinterpret_cast<const u32x4*>(p + 16);
-            af[i] = i32x8{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3],
-                          (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
-          }
+        for (int j = 0; j < NB; ++j)
+          bfr[slot][j] = *reinterpret_cast<const frag*>(
+              B + (wn * WTN + j * 32 + lrow) * kLds + s * 32 + lk * 16);
+      };
+      rd(0, 0);
 #pragma unroll
-          for (int j = 0; j < NB; ++j) {
-            const uint8_t* p = B + (wn * WTN + j * 32 + lrow) * kLds + s * 64 + lk * 32;
-            const u32x4 lo = *reinterpret_cast<const u32x4*>(p);
-            const u32x4 hi = *reinterpret_cast<const u32x4*>(p + 16);
-            bfr[j] = i32x8{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3],
-                           (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
-          }
+      for (int s = 0; s < 4; ++s) {  // 16 K per MFMA
+        if (s < 3) rd(s + 1, (s + 1) & 1);
 #pragma unroll
-          for (int i = 0; i < ML; ++i)
-#pragma unroll
-            for (int j = 0; j < NB; ++j)
-              acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
-                  af[i], bfr[j], acc[i][j], 0, 0, 0, 127, 0, 127);
-        }
-      } else {
-        using frag = bf16x8;
-        // fragments of sub-step s+1 are read while the MFMAs of sub-step s run
-        frag af[2][ML], bfr[2][NB];
-        auto rd = [&](int s, int slot) {
-#pragma unroll
-          for (int i = 0; i < ML; ++i)
-            af[slot][i] = *reinterpret_cast<const frag*>(
-                A + ((i * WM + wm) * 32 + lrow) * kLds + s * 32 + lk * 16);
+        for (int i = 0; i < ML; ++i)
 #pragma unroll
           for (int j = 0; j < NB; ++j)
-            bfr[slot][j] = *reinterpret_cast<const frag*>(
-                B + (wn * WTN + j * 32 + lrow) * kLds + s * 32 + lk * 16);
-        };
-        rd(0, 0);
-#pragma unroll
-        for (int s = 0; s < 4; ++s) {  // 16 K per MFMA
-          if (s < 3) rd(s + 1, (s + 1) & 1);
-#pragma unroll
-          for (int i = 0; i < ML; ++i)
-#pragma unroll
-            for (int j = 0; j < NB; ++j)
-              acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[s & 1][i], bfr[s & 1][j],
-                                                                  acc[i][j], 0, 0, 0);
-        }
+            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[s & 1][i], bfr[s & 1][j],
+                                                                acc[i][j], 0, 0, 0);
       }
     }
   };
@@ -861,12 +819,14 @@ struct PrefillTile<kNVFP4, STAGE> {
   static constexpr int BM = 128, BN = 128, WM = 1, WN = 4, NBUF = 2;
 };
 
-// decode batches: 32-row tiles, in the register-staged kernel (BF16, FP8) or
-// the direct-load kernel with three LDS buffers (NVFP4: packed codes in LDS
-// take a quarter of the expanded fp16 bytes, measured fastest)
+// decode batches: 32-row tiles, in the register-staged kernel (BF16, and the
+// FP8 up projection with its codes expanded on the way into LDS) or the
+// direct-load kernel with three LDS buffers (NVFP4: packed codes in LDS take
+// a quarter of the expanded fp16 bytes; the FP8 down projection: 2-3 % faster
+// than register staging at 4 and 64 tokens)
 constexpr int kDecodeRows = 32;
 constexpr int kDecodeMaxT = 512;
-constexpr int kNvDecodeBuffers = 3;
+constexpr int kDecodeBuffers = 3;
 
 // Below this many tokens the up projection touches so few experts that its
 // workgroups cannot be spread evenly over the CUs (about 2.3 per CU at four
@@ -879,9 +839,9 @@ constexpr int kNarrowUpMaxT = 16;
 
 template <int FMT, int STAGE>
 hipError_t launch_fmt_stage(int T, const GemmArgs& g, hipStream_t stream) {
-  if constexpr (FMT == kNVFP4) {
+  if constexpr (FMT == kNVFP4 || FMT == kFP8) {
     if (T < kDecodeMaxT)
-      return launch_dma<FMT, STAGE, kDecodeRows, 128, 1, 4, kNvDecodeBuffers>(g, stream);
+      return launch_dma<FMT, STAGE, kDecodeRows, 128, 1, 4, kDecodeBuffers>(g, stream);
   } else {
     if (STAGE == 0 && T < kNarrowUpMaxT) {
       if constexpr (FMT == kBF16) return launch_one<FMT, STAGE, kDecodeRows, 32, 1, 1>(g, stream);
