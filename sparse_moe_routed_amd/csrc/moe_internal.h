@@ -95,7 +95,7 @@ hipError_t launch_quant_fp8(const uint16_t* x, const int32_t* n_rows_dev, int ro
                             const uint32_t* amax, int mode, uint16_t* deq, uint8_t* codes,
                             float* scale, hipStream_t stream);
 // NVFP4: per 16-block codes and E4M3 scale; writes tensor scale to *scale.
-// mode 0: dequantised block values dec(q)*dec(sb) as bf16 into deq (may alias x);
+// mode 0: dequantised block values dec(q)*dec(sb) as fp16 into deq (may alias x);
 // mode 1: packed codes + block scales.
 hipError_t launch_quant_nvfp4(const uint16_t* x, const int32_t* n_rows_dev, int rows, int cols,
                               const uint32_t* amax, int mode, uint16_t* deq, uint8_t* codes,

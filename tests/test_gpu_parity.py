@@ -204,8 +204,9 @@ def test_forward_max_experts_and_k(wide, fmt, T):
 @pytest.mark.parametrize("fmt", ["bf16", "fp8", "nvfp4"])
 @pytest.mark.parametrize("T", [15, 16, 511])
 def test_forward_tile_regime_boundaries(full, fmt, T):
-    # 15 | 16: 64-column up-projection tiles below 16 tokens, 128-column from
-    # 16; 511: the largest batch on the 32-row decode tiles
+    # 15 | 16: narrow up-projection tiles below 16 tokens (32 columns for
+    # BF16, 64 for FP8), 128-column from 16; 511: the largest batch on the
+    # 32-row decode tiles
     _forward_case(full, fmt, T, outliers=T > 100)
 
 
