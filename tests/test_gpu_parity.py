@@ -410,6 +410,70 @@ def test_activation_codes_bit_exact(fmt, T):
     assert np.float32(scale.item()) == np.float32(s)
 
 
+def _fp8_special_values():
+    # amax 448 gives the tensor scale 1 exactly (448 / 448), so each code is
+    # the E4M3 encoding of the value itself: rounding midpoints (ties to the
+    # even code), one bf16 ulp either side of them, subnormals, -0 and values
+    # far below the smallest subnormal
+    v = [448.0, -448.0, 0.0, -0.0, 2.0 ** -6, -(2.0 ** -6), 2.0 ** -12, -(2.0 ** -12), 2.0 ** -133]
+    for m in range(8):  # [1, 2): spacing 1/8
+        mid = 1 + (2 * m + 1) / 16
+        v += [mid, -mid, mid + 2.0 ** -7, mid - 2.0 ** -7]
+    for m in range(6):  # [256, 448]: spacing 32
+        mid = 256 + 16 * (2 * m + 1)
+        v += [mid, -mid, mid + 2, mid - 2]
+    for m in range(8):  # subnormals m * 2^-9 and the midpoints between them
+        v += [m * 2.0 ** -9, (2 * m + 1) * 2.0 ** -10, -(2 * m + 1) * 2.0 ** -10]
+    v += [0.0] * (-len(v) % 64)
+    return v
+
+
+def _nvfp4_special_values():
+    # tensor amax 2688 gives S = 1; a block whose amax is 6 gets the block
+    # scale code of 1.0 and the multiplier 1, so its codes are the E2M1
+    # encodings of the values themselves
+    mids = [0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0]
+    a = [6.0] + mids + [-m for m in mids] + [-0.0]
+    b = [6.0, 0.25 + 2.0 ** -9, 0.75 - 2.0 ** -8, 1.25 + 2.0 ** -7, 1.75 - 2.0 ** -7,
+         2.5 + 2.0 ** -6, 3.5 - 2.0 ** -6, 5.0 + 2.0 ** -5, 5.0 - 2.0 ** -5, 0.0, 2.0 ** -20,
+         -(2.0 ** -20), -6.0, 4.0, 3.0, 0.5]
+    # block scale 448 (the largest E4M3 value): products v * fp32(1/448)
+    c = [2688.0, 1344.0, 112.0, 336.0, 560.0, -784.0, 1120.0, -1568.0, 2240.0, 0.0, -0.0,
+         1.0, -1.0, 100.0, 2000.0, -2688.0]
+    d = [0.0] * 16  # all zero: block scale code 0
+    # amax / 6 = 2^-11 is below half the smallest E4M3 subnormal: scale code
+    # 0, so the whole block is zero
+    e = [6 * 2.0 ** -11, 3 * 2.0 ** -11, -(2.0 ** -11)] + [2.0 ** -12] * 13
+    # amax / 6 = 5 * 2^-9, a subnormal block scale
+    f = [30 * 2.0 ** -9, 15 * 2.0 ** -9, -7 * 2.0 ** -9, 2.0 ** -9] + [3 * 2.0 ** -10] * 12
+    v = a + b + c + d + e + f
+    v += [0.0] * (-len(v) % 64)
+    return v
+
+
+@pytest.mark.parametrize("fmt", ["fp8", "nvfp4"])
+def test_activation_codes_special_values(fmt):
+    # the hardware converts behind the quantisers at rounding ties, -0,
+    # subnormals and saturation, against the oracle's encoders
+    vals = _fp8_special_values() if fmt == "fp8" else _nvfp4_special_values()
+    x = torch.tensor(vals, dtype=torch.float32).reshape(-1, 64)
+    xb = x.to(torch.bfloat16)
+    assert torch.equal(xb.float(), x)  # every value is a bf16 value
+    codes, bs, scale = moe.quantize_activation(xb.cuda(), fmt)
+    torch.cuda.synchronize()
+    xf = x.numpy()
+    if fmt == "fp8":
+        q, s = codecs.fp8_quantize(xf)
+        assert np.float32(s) == np.float32(1.0)
+        assert np.array_equal(codes.cpu().numpy(), q)
+    else:
+        q, sb, s = codecs.nvfp4_quantize(xf)
+        assert np.float32(s) == np.float32(1.0)
+        assert np.array_equal(codes.cpu().numpy(), codecs.nvfp4_pack(q))
+        assert np.array_equal(bs.cpu().numpy(), sb)
+    assert np.float32(scale.item()) == np.float32(s)
+
+
 # --------------------------------------------------------------------------- stacked path
 def test_prenorm_and_residual(full):
     x = _x(64, FULL, outliers=True)
