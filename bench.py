@@ -11,7 +11,11 @@ layers with pre-norm and residual.  Inputs are resident in HBM before timing.
 W untimed warm-up steps, then exactly K steps between two device
 synchronisations, with no events.  Per-stage durations come from a second
 pass of K steps with HIP events recorded at every stage boundary on the
-stream the kernels run on.
+stream the kernels run on; before each of those steps a 512 MB buffer is
+read outside the events, so no step finds the previous step's weights in the
+256 MB Infinity Cache.  A third pass records one event before and one after
+each step (the same read before each): `step_ms_events` gives the p10 / p50 /
+p90 of those step times.
 
 Prints one JSON line.  `roofline` describes the dominant kernel (algorithmic
 bytes or flops per launch / its mean duration); `cpu_baseline` is the CPU
@@ -196,10 +200,16 @@ def main():
     # (stacked workloads: events around every layer, averaged over the layers)
     timed_stages = True
     stage_ms = {}
+    # Before each step a 512 MB buffer is read (outside the events), more than
+    # the 256 MB Infinity Cache, so no step finds the previous step's weights
+    # in it.  Reading leaves clean lines; writing would leave dirty ones whose
+    # write-back the next kernel would pay for.
     evs = [[([hip.event(), hip.event()], [hip.event() for _ in range(n_ev)])
             for _ in range(n_layers)] for _ in range(args.steps)]
+    flush = torch.ones(128 << 20, dtype=torch.float32, device=dev)
     torch.cuda.synchronize()
     for i in range(args.steps):
+        flush.amax()
         step(evs[i])
     torch.cuda.synchronize()
     flat = [e for per_step in evs for e in per_step]
@@ -210,7 +220,25 @@ def main():
         for h in er + es:
             hip.destroy(h)
 
-    # pass 3 (optional): the same step captured once into a HIP graph (the
+    # pass 3: the distribution of single-step times, with one event before and
+    # one after each step (and the cache-clearing read before the first)
+    ev2 = [(hip.event(), hip.event()) for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    for i in range(args.steps):
+        flush.amax()
+        hip.record(ev2[i][0], stream)
+        step()
+        hip.record(ev2[i][1], stream)
+    torch.cuda.synchronize()
+    del flush
+    step_ev = sorted(hip.elapsed(a, b) for a, b in ev2)
+    for a, b in ev2:
+        hip.destroy(a)
+        hip.destroy(b)
+    q = lambda p: step_ev[min(len(step_ev) - 1, int(round(p * (len(step_ev) - 1))))]
+    step_pct = {"p10": round(q(0.1), 4), "p50": round(q(0.5), 4), "p90": round(q(0.9), 4)}
+
+    # pass 4 (optional): the same step captured once into a HIP graph (the
     # library's calls hold no host sync, allocation or memset), K replays
     # between two synchronisations
     graph_rec = None
@@ -293,6 +321,7 @@ def main():
         "layer_tflops": round(2 * flops_up / (layer_ms * 1e-3) / 1e12, 2),
         "experts_touched": touched,
         "stage_ms": {k2: round(v, 4) for k2, v in stage_ms.items()},
+        "step_ms_events": step_pct,
         "roofline": roof,
     }
     if graph_rec:
