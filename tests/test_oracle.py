@@ -10,7 +10,6 @@ import math
 import os
 
 import numpy as np
-import pytest
 import torch
 
 from oracle import codecs
