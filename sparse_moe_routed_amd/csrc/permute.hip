@@ -177,7 +177,7 @@ __device__ void scatter_chunk(const int (&ev)[kRounds], const float* __restrict_
 }
 
 __global__ __launch_bounds__(kPermThreads) void perm_scatter_kernel(
-    const int32_t* __restrict__ ids, const float* __restrict__ gates, int R, int E, int k,
+    const int32_t* __restrict__ ids, const float* __restrict__ gates, int R, int E,
     const int32_t* __restrict__ chunk_base, const int32_t* __restrict__ offsets,
     int32_t* __restrict__ sorted_src, int32_t* __restrict__ inv,
     float* __restrict__ row_gate) {
@@ -241,7 +241,7 @@ hipError_t launch_permute(const int32_t* ids, const float* gates, int T, int E, 
                      p.chunk_counts, n_chunks, E, p.chunk_base, p.counts, p.offsets, p.bm0,
                      p.tile_off0, p.bm1, p.tile_off1, p.zero_words, p.n_zero);
   hipLaunchKernelGGL(perm_scatter_kernel, dim3(n_chunks), dim3(kPermThreads), 0, stream, ids,
-                     gates, R, E, k, p.chunk_base, p.offsets, p.sorted_src, p.inv, p.row_gate);
+                     gates, R, E, p.chunk_base, p.offsets, p.sorted_src, p.inv, p.row_gate);
   return hipGetLastError();
 }
 
