@@ -15,15 +15,20 @@
  *
  * Conventions for every call:
  *   - Pointers marked [dev] are device pointers (hipMalloc or torch CUDA
- *     tensors); [host] are host pointers read during the call only.
+ *     tensors); [host] are host pointers read during the call only (except
+ *     a cache's host bank, which its uploads read from `stream` later: keep
+ *     it unchanged while they may be in flight).
  *   - All device work is enqueued asynchronously on `stream` (a hipStream_t;
- *     NULL = the null stream).  No call synchronises with the host.
+ *     NULL = the null stream).  No call synchronises with the host, except
+ *     moe_cache_init and moe_forward_cached, which wait for `stream`.
  *   - Row-major, contiguous layouts, except the packed NVFP4 expert bank
  *     (128-row panels, see moe_experts); bf16 is passed as raw 16-bit words.
  *   - The caller owns every buffer.  The library allocates no device memory;
  *     scratch comes from the caller's workspace (moe_workspace_size).
  *   - Arguments are validated on the host before any launch.  On error the
- *     call returns a non-zero moe_status and enqueues nothing.  T == 0 is a
+ *     call returns a non-zero moe_status and enqueues nothing (one
+ *     exception: moe_forward_cached reports a batch that selects more
+ *     experts than the cache holds after its permutation).  T == 0 is a
  *     valid no-op.  A failed launch returns MOE_EHIP.
  *   - Calls are reentrant; calls that share a workspace must be ordered on
  *     one stream.  Non-finite inputs give undefined (but memory-safe)
@@ -43,7 +48,7 @@
 extern "C" {
 #endif
 
-#define MOE_ABI_VERSION 3
+#define MOE_ABI_VERSION 4
 
 typedef enum {
   MOE_OK = 0,
@@ -172,6 +177,68 @@ int32_t moe_forward_timed(const moe_dims* dims, int32_t T, const void* x,
                           const moe_experts* experts, void* y, int32_t y_dtype,
                           void* ws, size_t ws_bytes, void* stream,
                           void* const* events, int32_t n_events);
+
+/* ---- expert residency split
+ * The routed expert banks stay in host memory in their stored format; the
+ * experts a batch selects are uploaded into a bounded cache of device slots,
+ * and experts that keep being selected stay resident.  The cache must cover
+ * the experts selected together and cannot exceed the expert count
+ * (audio.cpp notes "NVIDIA Nemotron 3.5 Transcribe", section "CPU weight
+ * offload").  Here a batch's touched experts must fit the slots; the least
+ * recently used resident experts the batch does not touch are replaced.
+ * All memory is the caller's:
+ *   host      the whole bank in host memory, layouts as moe_experts (fmt, up,
+ *             down, up_bs, down_bs; pinned memory lets the uploads run as
+ *             asynchronous DMA); its scale pointers are not used
+ *   up_s, down_s  [dev] fp32 [E] per-expert scales (FP8/NVFP4), resident
+ *   slot_up, slot_down        [dev] n_slots experts of codes, same
+ *             per-expert layout and size as the bank
+ *   slot_up_bs, slot_down_bs  [dev] NVFP4 block scales of the slots
+ *   slot_of   [dev] int32 [E]: the slot of each expert, written by the library
+ *   state     [host] moe_cache_state_size bytes of replacement state,
+ *             8-byte aligned, kept by the caller between calls */
+typedef struct {
+  int32_t n_slots;
+  moe_experts host;
+  const float* up_s;
+  const float* down_s;
+  void* slot_up;
+  void* slot_down;
+  uint8_t* slot_up_bs;
+  uint8_t* slot_down_bs;
+  int32_t* slot_of;
+} moe_cache;
+
+/* [host] per-call counters of moe_forward_cached */
+typedef struct {
+  int32_t touched;          /* experts the batch selected              */
+  int32_t hits;             /* of them, already resident               */
+  int32_t misses;           /* of them, uploaded by this call          */
+  int64_t bytes_uploaded;   /* host-to-device bytes of those uploads   */
+} moe_cache_stats;
+
+/* Host bytes of replacement state for n_slots slots (top_k <= n_slots <= E);
+ * 0 for invalid arguments. */
+size_t moe_cache_state_size(const moe_dims* dims, int32_t n_slots);
+
+/* Marks every slot empty (state, and slot_of on `stream`, which the call
+ * waits for).  MOE_EINVAL for null pointers, n_slots outside
+ * [top_k, n_experts] or a too small state. */
+int32_t moe_cache_init(const moe_dims* dims, const moe_cache* cache, void* state,
+                       size_t state_bytes, void* stream);
+
+/* moe_forward with the expert weights taken from the cache.  After the
+ * permutation it copies the per-expert row counts to the host and waits for
+ * the stream (the uploads depend on the routing), uploads the missing
+ * experts, updates slot_of and runs the expert GEMMs on the slots; y equals
+ * moe_forward's on the same bank bit for bit.  If the batch selects more
+ * experts than there are slots it returns MOE_EUNSUPPORTED after the
+ * permutation, with nothing uploaded and y not written.  Not capturable in a
+ * HIP graph (it waits for the stream).  stats [host] may be NULL. */
+int32_t moe_forward_cached(const moe_dims* dims, int32_t T, const void* x,
+                           const int32_t* ids, const float* gates, const moe_cache* cache,
+                           void* state, void* y, int32_t y_dtype, void* ws, size_t ws_bytes,
+                           void* stream, moe_cache_stats* stats);
 
 /* Byte offsets of stage results inside a moe_forward workspace (for tests and
  * tools; -1 where a stage does not exist for the format). */

@@ -48,6 +48,18 @@ class Experts(ctypes.Structure):
                 ("up_s", ctypes.c_void_p), ("down_s", ctypes.c_void_p)]
 
 
+class Cache(ctypes.Structure):
+    _fields_ = [("n_slots", ctypes.c_int32), ("host", Experts), ("up_s", ctypes.c_void_p),
+                ("down_s", ctypes.c_void_p), ("slot_up", ctypes.c_void_p),
+                ("slot_down", ctypes.c_void_p), ("slot_up_bs", ctypes.c_void_p),
+                ("slot_down_bs", ctypes.c_void_p), ("slot_of", ctypes.c_void_p)]
+
+
+class CacheStats(ctypes.Structure):
+    _fields_ = [("touched", ctypes.c_int32), ("hits", ctypes.c_int32), ("misses", ctypes.c_int32),
+                ("bytes_uploaded", ctypes.c_int64)]
+
+
 class WsLayout(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int64) for n in
                 ("counts", "offsets", "sorted_src", "inv", "act", "out_rows", "x_q", "act_q",
@@ -76,6 +88,14 @@ _SIGS = {
                                            ctypes.c_void_p, ctypes.c_int32, ctypes.c_void_p,
                                            ctypes.c_size_t, ctypes.c_void_p,
                                            ctypes.POINTER(ctypes.c_void_p), ctypes.c_int32]),
+    "moe_cache_state_size": (ctypes.c_size_t, [ctypes.POINTER(Dims), ctypes.c_int32]),
+    "moe_cache_init": (ctypes.c_int32, [ctypes.POINTER(Dims), ctypes.POINTER(Cache), ctypes.c_void_p,
+                                        ctypes.c_size_t, ctypes.c_void_p]),
+    "moe_forward_cached": (ctypes.c_int32, [ctypes.POINTER(Dims), ctypes.c_int32, ctypes.c_void_p,
+                                            ctypes.c_void_p, ctypes.c_void_p, ctypes.POINTER(Cache),
+                                            ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int32,
+                                            ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p,
+                                            ctypes.POINTER(CacheStats)]),
     "moe_quantize_experts": (ctypes.c_int32, [ctypes.POINTER(Dims), ctypes.c_int32, ctypes.c_void_p,
                                               ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
                                               ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
@@ -93,7 +113,7 @@ _SIGS = {
 }
 
 _lib = None
-ABI_VERSION = 3  # MOE_ABI_VERSION of include/moe.h this binding describes
+ABI_VERSION = 4  # MOE_ABI_VERSION of include/moe.h this binding describes
 
 
 def lib():
@@ -294,6 +314,75 @@ def forward_timed(x: torch.Tensor, ids: torch.Tensor, gates: torch.Tensor, exper
         ctypes.byref(d), T, _ptr(x), _ptr(ids), _ptr(gates), ctypes.byref(e), _ptr(y), yd,
         _ptr(ws), ws.numel(), _stream(), arr, len(events)))
     return y
+
+
+class ExpertCache:
+    """moe_cache: the bank's codes in pinned host memory and n_slots device
+    slots that hold the experts batches select (least recently used replaced).
+    Per-expert scales stay on the device."""
+
+    def __init__(self, bank: ExpertBank, n_slots: int, dims: LayerDims = LayerDims()):
+        dev = bank.up.device
+
+        def host(t):
+            if t is None:
+                return None
+            h = torch.empty(t.shape, dtype=t.dtype, pin_memory=True)
+            h.copy_(t)
+            return h
+
+        def slots(t):
+            return None if t is None else torch.empty((n_slots,) + tuple(t.shape[1:]), dtype=t.dtype,
+                                                       device=dev)
+
+        self.fmt, self.n_slots, self.dims = bank.fmt, int(n_slots), dims
+        self.host_up, self.host_down = host(bank.up), host(bank.down)
+        self.host_up_bs, self.host_down_bs = host(bank.up_bs), host(bank.down_bs)
+        self.up_s, self.down_s = bank.up_s, bank.down_s
+        self.slot_up, self.slot_down = slots(bank.up), slots(bank.down)
+        self.slot_up_bs, self.slot_down_bs = slots(bank.up_bs), slots(bank.down_bs)
+        self.slot_of = torch.empty(dims.n_experts, dtype=torch.int32, device=dev)
+        d = dims.c()
+        self.state_bytes = int(lib().moe_cache_state_size(ctypes.byref(d), self.n_slots))
+        if self.state_bytes == 0:
+            raise ValueError(f"n_slots {n_slots} outside [top_k, n_experts]")
+        self.state = (ctypes.c_uint64 * ((self.state_bytes + 7) // 8))()  # 8-byte aligned
+        c = self.c()
+        _check("moe_cache_init", lib().moe_cache_init(ctypes.byref(d), ctypes.byref(c), self.state,
+                                                      self.state_bytes, _stream()))
+
+    def c(self) -> Cache:
+        p = lambda t: t.data_ptr() if t is not None else None
+        h = Experts(WFMT[self.fmt], p(self.host_up), p(self.host_down), p(self.host_up_bs),
+                    p(self.host_down_bs), None, None)
+        return Cache(self.n_slots, h, p(self.up_s), p(self.down_s), p(self.slot_up),
+                     p(self.slot_down), p(self.slot_up_bs), p(self.slot_down_bs), p(self.slot_of))
+
+
+def forward_cached(x: torch.Tensor, ids: torch.Tensor, gates: torch.Tensor, cache: ExpertCache,
+                   dims: LayerDims = LayerDims(), y_dtype: torch.dtype = torch.float32,
+                   ws: Optional[torch.Tensor] = None, y: Optional[torch.Tensor] = None):
+    """moe_forward_cached: (y [T, H], stats dict); y equals forward() on the
+    bank the cache was built from."""
+    T = x.shape[0]
+    _dev(x, torch.bfloat16, "x", (T, dims.hidden))
+    _dev(ids, torch.int32, "ids", (T, dims.top_k))
+    _dev(gates, torch.float32, "gates", (T, dims.top_k))
+    if ws is None:
+        ws = workspace(dims, cache.fmt, T, x.device)
+    _dev(ws, torch.uint8, "ws")
+    if y is None:
+        y = torch.empty((T, dims.hidden), dtype=y_dtype, device=x.device)
+    _dev(y, y_dtype, "y", (T, dims.hidden))
+    yd = {torch.float32: Y_F32, torch.bfloat16: Y_BF16}[y_dtype]
+    d = dims.c()
+    c = cache.c()
+    st = CacheStats()
+    _check("moe_forward_cached", lib().moe_forward_cached(
+        ctypes.byref(d), T, _ptr(x), _ptr(ids), _ptr(gates), ctypes.byref(c), cache.state, _ptr(y),
+        yd, _ptr(ws), ws.numel(), _stream(), ctypes.byref(st)))
+    return y, {"touched": st.touched, "hits": st.hits, "misses": st.misses,
+               "bytes_uploaded": st.bytes_uploaded}
 
 
 def quantize_experts(up: torch.Tensor, down: torch.Tensor, fmt: str,

@@ -126,6 +126,8 @@ __global__ __launch_bounds__(WM* WN * 64) void grouped_gemm_kernel(GemmArgs g) {
   const int row0 = g.offsets[e] + mt * BM;
   const int rows_valid = min(BM, g.offsets[e + 1] - row0);
   const int n0 = ntile * BN;
+  // where the expert's weights sit: its own index, or its device cache slot
+  const int ew = g.w_slot ? g.w_slot[e] : e;
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave / WN, wn = wave % WN;
@@ -158,13 +160,13 @@ __global__ __launch_bounds__(WM* WN * 64) void grouped_gemm_kernel(GemmArgs g) {
     if constexpr (FMT == kFP8X) {
       const int r = c >> 2, q = c & 3;  // 16 codes of the row's 64 per step
       const int n = min(n0 + r, N - 1);
-      const size_t row = static_cast<size_t>(e) * N + n;
+      const size_t row = static_cast<size_t>(ew) * N + n;
       b_src[i] = static_cast<const uint8_t*>(g.b) + row * K + q * 16;
       b_dst[i] = r * kLds + q * 32;
     } else {
       const int r = c >> 3, cc = c & 7;
       const int n = min(n0 + r, N - 1);
-      const size_t row = static_cast<size_t>(e) * N + n;
+      const size_t row = static_cast<size_t>(ew) * N + n;
       b_src[i] = static_cast<const uint8_t*>(g.b) + row * k_bytes + cc * 16;
       b_dst[i] = r * kLds + cc * 16;
     }
@@ -441,6 +443,8 @@ __global__ __launch_bounds__(WM* WN * 64) void grouped_gemm_dma_kernel(GemmArgs 
   const int row0 = g.offsets[e] + mt * BM;
   const int rows_valid = min(BM, g.offsets[e + 1] - row0);
   const int n0 = ntile * BN;
+  // where the expert's weights sit: its own index, or its device cache slot
+  const int ew = g.w_slot ? g.w_slot[e] : e;
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave / WN, wn = wave % WN;
@@ -486,10 +490,10 @@ __global__ __launch_bounds__(WM* WN * 64) void grouped_gemm_dma_kernel(GemmArgs 
     const int c = (lane % CPR) ^ lds_swz<RB>(r);
     const int n = min(n0 + r, N - 1);
     if constexpr (FMT == kNVFP4) {
-      b_src[q] = static_cast<const uint8_t*>(g.b) + (static_cast<size_t>(e) * N + nv_pn0) * w_bytes +
+      b_src[q] = static_cast<const uint8_t*>(g.b) + (static_cast<size_t>(ew) * N + nv_pn0) * w_bytes +
                  (n - nv_pn0) * RB + c * 16;
     } else {
-      b_src[q] = static_cast<const uint8_t*>(g.b) + (static_cast<size_t>(e) * N + n) * w_bytes + c * 16;
+      b_src[q] = static_cast<const uint8_t*>(g.b) + (static_cast<size_t>(ew) * N + n) * w_bytes + c * 16;
     }
     b_dst[q] = B_OFF + qi * 1024;
     b_cof[q] = c * 16;
@@ -501,7 +505,7 @@ __global__ __launch_bounds__(WM* WN * 64) void grouped_gemm_dma_kernel(GemmArgs 
     for (int q = 0; q < QS; ++q) {
       const int qi = (wave + q * NW) % NSC;
       const int n = min(n0 + qi * 64 + lane, N - 1);
-      s_src[q] = g.b_bs + (static_cast<size_t>(e) * N + nv_pn0) * (K / 16) + (n - nv_pn0) * 4;
+      s_src[q] = g.b_bs + (static_cast<size_t>(ew) * N + nv_pn0) * (K / 16) + (n - nv_pn0) * 4;
       s_dst[q] = S_OFF + qi * 256;
     }
   }

@@ -90,6 +90,77 @@ T* at(void* ws, size_t off) {
 
 moe_status hip_status(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_EHIP; }
 
+// ---- expert cache: replacement state in the caller's host buffer
+constexpr uint32_t kCacheMagic = 0x4d6f4543u;
+
+struct CacheHeader {
+  uint32_t magic;
+  int32_t n_experts, n_slots, fmt;
+  int64_t tick;
+};
+
+// views of the state buffer: header, then slot -> expert, expert -> slot,
+// last use of each expert, and host staging for the per-expert row counts
+// (device to host) and the slot map (host to device)
+struct CacheView {
+  CacheHeader* h;
+  int32_t* slot_expert;  // [n_slots], -1 = empty
+  int32_t* expert_slot;  // [E], -1 = not resident
+  int64_t* last_use;     // [E]
+  int32_t* counts;       // [E]
+  int32_t* slot_of;      // [E], the device map's host copy
+};
+
+size_t cache_state_bytes(int E, int n_slots) {
+  return sizeof(CacheHeader) + static_cast<size_t>(n_slots) * 4 + static_cast<size_t>(E) * (4 + 8 + 4 + 4);
+}
+
+CacheView cache_view(void* state, int E, int n_slots) {
+  uint8_t* p = static_cast<uint8_t*>(state);
+  CacheView v;
+  v.h = reinterpret_cast<CacheHeader*>(p);
+  p += sizeof(CacheHeader);
+  v.last_use = reinterpret_cast<int64_t*>(p);  // 8-byte fields first (header size is a multiple of 8)
+  p += static_cast<size_t>(E) * 8;
+  v.slot_expert = reinterpret_cast<int32_t*>(p);
+  p += static_cast<size_t>(n_slots) * 4;
+  v.expert_slot = reinterpret_cast<int32_t*>(p);
+  p += static_cast<size_t>(E) * 4;
+  v.counts = reinterpret_cast<int32_t*>(p);
+  p += static_cast<size_t>(E) * 4;
+  v.slot_of = reinterpret_cast<int32_t*>(p);
+  return v;
+}
+
+// bytes of one expert's codes and (NVFP4) block scales in a projection N x K
+size_t expert_code_bytes(int fmt, int N, int K) {
+  const size_t n = static_cast<size_t>(N) * K;
+  return fmt == kBF16 ? 2 * n : (fmt == kFP8 ? n : n / 2);
+}
+size_t expert_scale_bytes(int fmt, int N, int K) {
+  return fmt == kNVFP4 ? static_cast<size_t>(N) * K / 16 : 0;
+}
+
+moe_status cache_check(const moe_dims* d, const moe_cache* c) {
+  if (!c) return MOE_EINVAL;
+  if (!fmt_ok(c->host.fmt)) return MOE_EINVAL;
+  if (c->n_slots < d->top_k || c->n_slots > d->n_experts) return MOE_EINVAL;
+  if (!c->host.up || !c->host.down || !c->slot_up || !c->slot_down || !c->slot_of)
+    return MOE_EINVAL;
+  if (c->host.fmt != kBF16 && (!c->up_s || !c->down_s)) return MOE_EINVAL;
+  if (c->host.fmt == kNVFP4 &&
+      (!c->host.up_bs || !c->host.down_bs || !c->slot_up_bs || !c->slot_down_bs))
+    return MOE_EINVAL;
+  return MOE_OK;
+}
+
+// what a cached forward needs besides forward_impl's arguments
+struct CacheCall {
+  const moe_cache* cache;
+  void* state;
+  moe_cache_stats* stats;
+};
+
 }  // namespace
 
 extern "C" {
@@ -126,6 +197,38 @@ int32_t moe_workspace_layout(const moe_dims* dims, int32_t fmt, int32_t T, moe_w
   out->scales = static_cast<int64_t>(L.scales);
   out->total = static_cast<int64_t>(L.total);
   return MOE_OK;
+}
+
+size_t moe_cache_state_size(const moe_dims* dims, int32_t n_slots) {
+  if (!dims_ok(dims) || n_slots < dims->top_k || n_slots > dims->n_experts) return 0;
+  return cache_state_bytes(dims->n_experts, n_slots);
+}
+
+int32_t moe_cache_init(const moe_dims* dims, const moe_cache* cache, void* state,
+                       size_t state_bytes, void* stream) {
+  if (const moe_status ds = dims_check(dims)) return ds;
+  if (const moe_status cs = cache_check(dims, cache)) return cs;
+  const int E = dims->n_experts, S = cache->n_slots;
+  if (!state || state_bytes < cache_state_bytes(E, S) || reinterpret_cast<uintptr_t>(state) % 8)
+    return MOE_EINVAL;
+  const CacheView v = cache_view(state, E, S);
+  v.h->magic = kCacheMagic;
+  v.h->n_experts = E;
+  v.h->n_slots = S;
+  v.h->fmt = cache->host.fmt;
+  v.h->tick = 0;
+  for (int i = 0; i < S; ++i) v.slot_expert[i] = -1;
+  for (int e = 0; e < E; ++e) {
+    v.expert_slot[e] = -1;
+    v.last_use[e] = -1;
+    v.counts[e] = 0;
+    v.slot_of[e] = -1;
+  }
+  const hipStream_t st = static_cast<hipStream_t>(stream);
+  if (hipMemcpyAsync(cache->slot_of, v.slot_of, static_cast<size_t>(E) * 4,
+                     hipMemcpyHostToDevice, st) != hipSuccess)
+    return MOE_EHIP;
+  return hip_status(hipStreamSynchronize(st));
 }
 
 size_t moe_route_workspace_size(const moe_dims* dims, int32_t max_tokens) {
@@ -175,11 +278,34 @@ struct StageMarks {
   }
 };
 
+// The forward pass.  With `cc` set, the expert weights come from the cache:
+// after the permutation the row counts go to the host, the missing experts
+// are uploaded into slots, and the GEMMs read the slots through slot_of.
 int32_t forward_impl(const moe_dims* dims, int32_t T, const void* x, const int32_t* ids,
-                     const float* gates, const moe_experts* ex, void* y, int32_t y_dtype,
+                     const float* gates, const moe_experts* ex_in, void* y, int32_t y_dtype,
                      void* ws, size_t ws_bytes, void* stream, void* const* events,
-                     int32_t n_events) {
+                     int32_t n_events, const CacheCall* cc = nullptr) {
   if (const moe_status ds = dims_check(dims)) return ds;
+  moe_experts cached_bank{};
+  const moe_experts* ex = ex_in;
+  if (cc) {
+    if (const moe_status cs = cache_check(dims, cc->cache)) return cs;
+    const moe_cache* c = cc->cache;
+    if (!cc->state || reinterpret_cast<uintptr_t>(cc->state) % 8) return MOE_EINVAL;
+    const CacheHeader* h = static_cast<const CacheHeader*>(cc->state);
+    if (h->magic != kCacheMagic || h->n_experts != dims->n_experts || h->n_slots != c->n_slots ||
+        h->fmt != c->host.fmt)
+      return MOE_EINVAL;  // not initialised by moe_cache_init for this cache
+    cached_bank.fmt = c->host.fmt;
+    cached_bank.up = c->slot_up;
+    cached_bank.down = c->slot_down;
+    cached_bank.up_bs = c->slot_up_bs;
+    cached_bank.down_bs = c->slot_down_bs;
+    cached_bank.up_s = c->up_s;
+    cached_bank.down_s = c->down_s;
+    ex = &cached_bank;
+    if (cc->stats) *cc->stats = moe_cache_stats{0, 0, 0, 0};
+  }
   if (!ex) return MOE_EINVAL;
   if (T < 0 || T > kMaxTokens) return MOE_EINVAL;
   if (!fmt_ok(ex->fmt)) return MOE_EINVAL;
@@ -221,6 +347,79 @@ int32_t forward_impl(const moe_dims* dims, int32_t T, const void* x, const int32
   hipError_t err = moe::launch_permute(ids, gates, T, E, k, p, st);
   if (err != hipSuccess) return MOE_EHIP;
 
+  // 1b. cached weights: bring the experts this batch touches into slots
+  const int32_t* w_slot = nullptr;
+  if (cc) {
+    const moe_cache* c = cc->cache;
+    const int S = c->n_slots;
+    const CacheView v = cache_view(cc->state, E, S);
+    if (hipMemcpyAsync(v.counts, p.counts, static_cast<size_t>(E) * 4, hipMemcpyDeviceToHost,
+                       st) != hipSuccess ||
+        hipStreamSynchronize(st) != hipSuccess)
+      return MOE_EHIP;
+    int touched = 0;
+    for (int e = 0; e < E; ++e) touched += v.counts[e] > 0;
+    if (touched > S) return MOE_EUNSUPPORTED;
+    const int64_t now = ++v.h->tick;
+    int hits = 0, misses = 0;
+    int64_t bytes = 0;
+    const size_t up_b = expert_code_bytes(fmt, F, H), down_b = expert_code_bytes(fmt, H, F);
+    const size_t up_sb = expert_scale_bytes(fmt, F, H), down_sb = expert_scale_bytes(fmt, H, F);
+    for (int e = 0; e < E; ++e) {
+      if (v.counts[e] <= 0) continue;
+      if (v.expert_slot[e] >= 0) {
+        ++hits;
+        v.last_use[e] = now;
+        continue;
+      }
+      // a free slot, else the least recently used resident expert this
+      // batch does not touch (touched experts are stamped `now`)
+      int slot = -1;
+      int64_t oldest = now;
+      for (int i = 0; i < S && slot < 0; ++i)
+        if (v.slot_expert[i] < 0) slot = i;
+      if (slot < 0) {
+        for (int i = 0; i < S; ++i) {
+          const int r = v.slot_expert[i];
+          if (v.counts[r] <= 0 && v.last_use[r] < oldest) {
+            oldest = v.last_use[r];
+            slot = i;
+          }
+        }
+      }
+      if (slot < 0) return MOE_EHIP;  // cannot happen: touched <= S
+      if (v.slot_expert[slot] >= 0) {
+        v.expert_slot[v.slot_expert[slot]] = -1;
+        v.slot_of[v.slot_expert[slot]] = -1;
+      }
+      v.slot_expert[slot] = e;
+      v.expert_slot[e] = slot;
+      v.slot_of[e] = slot;
+      v.last_use[e] = now;
+      ++misses;
+      auto up_src = static_cast<const uint8_t*>(c->host.up) + static_cast<size_t>(e) * up_b;
+      auto down_src = static_cast<const uint8_t*>(c->host.down) + static_cast<size_t>(e) * down_b;
+      hipError_t ce = hipMemcpyAsync(static_cast<uint8_t*>(c->slot_up) + slot * up_b, up_src, up_b,
+                                     hipMemcpyHostToDevice, st);
+      if (ce == hipSuccess)
+        ce = hipMemcpyAsync(static_cast<uint8_t*>(c->slot_down) + slot * down_b, down_src, down_b,
+                            hipMemcpyHostToDevice, st);
+      if (ce == hipSuccess && up_sb)
+        ce = hipMemcpyAsync(c->slot_up_bs + slot * up_sb, c->host.up_bs + e * up_sb, up_sb,
+                            hipMemcpyHostToDevice, st);
+      if (ce == hipSuccess && down_sb)
+        ce = hipMemcpyAsync(c->slot_down_bs + slot * down_sb, c->host.down_bs + e * down_sb,
+                            down_sb, hipMemcpyHostToDevice, st);
+      if (ce != hipSuccess) return MOE_EHIP;
+      bytes += static_cast<int64_t>(up_b + down_b + up_sb + down_sb);
+    }
+    if (hipMemcpyAsync(c->slot_of, v.slot_of, static_cast<size_t>(E) * 4, hipMemcpyHostToDevice,
+                       st) != hipSuccess)
+      return MOE_EHIP;
+    w_slot = c->slot_of;
+    if (cc->stats) *cc->stats = moe_cache_stats{touched, hits, misses, bytes};
+  }
+
   // 2. token quantisation (fp8 / nvfp4)
   marks.mark(1);
   const void* a_up = x;
@@ -258,6 +457,7 @@ int32_t forward_impl(const moe_dims* dims, int32_t T, const void* x, const int32
   g.out = at<uint16_t>(ws, L.act);
   g.row_gate = nullptr;
   g.amax = amax_a;
+  g.w_slot = w_slot;
   err = moe::launch_gemm(fmt, 0, T, g, st);
   if (err != hipSuccess) return MOE_EHIP;
 
@@ -317,6 +517,15 @@ int32_t moe_forward_timed(const moe_dims* dims, int32_t T, const void* x, const 
   if (!events || n_events < MOE_N_STAGES + 1) return MOE_EINVAL;
   return forward_impl(dims, T, x, ids, gates, ex, y, y_dtype, ws, ws_bytes, stream, events,
                       n_events);
+}
+
+int32_t moe_forward_cached(const moe_dims* dims, int32_t T, const void* x, const int32_t* ids,
+                           const float* gates, const moe_cache* cache, void* state, void* y,
+                           int32_t y_dtype, void* ws, size_t ws_bytes, void* stream,
+                           moe_cache_stats* stats) {
+  const CacheCall cc{cache, state, stats};
+  return forward_impl(dims, T, x, ids, gates, nullptr, y, y_dtype, ws, ws_bytes, stream, nullptr, 0,
+                      &cc);
 }
 
 int32_t moe_quantize_experts(const moe_dims* dims, int32_t fmt, const void* up_bf16,

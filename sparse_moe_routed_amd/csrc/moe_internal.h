@@ -69,6 +69,8 @@ struct GemmArgs {
                               // in kNvPanel-row panels, K-step-major)
   const uint8_t* b_bs;        // nvfp4 block scales, N*K/16 bytes per expert, same panels
   const float* b_s;           // fp8 / nvfp4 weight scale per expert [E]
+  const int32_t* w_slot;      // [E] slot of each expert's weights in b / b_bs, or null:
+                              // expert e at index e (resident bank)
   const float* a_s;           // fp8 / nvfp4 activation scale (device scalar)
   int N, K;
   void* out;                  // up: bf16 [R, N]; down: fp32 [R, N]

@@ -147,6 +147,42 @@ def test_forward_validation(lib):
     assert call(T=0, ws=None, wsb=0) == moe.OK
 
 
+def test_cache_validation(lib):
+    d = _dims()
+    assert lib.moe_cache_state_size(ctypes.byref(d), 5) == 0    # fewer slots than top_k
+    assert lib.moe_cache_state_size(ctypes.byref(d), 129) == 0  # more slots than experts
+    assert lib.moe_cache_state_size(None, 32) == 0
+    n = lib.moe_cache_state_size(ctypes.byref(d), 32)
+    assert n > 0
+    state = (ctypes.c_uint64 * (n // 8 + 1))()
+    host = moe.Experts(0, FAKE.value, FAKE.value, None, None, None, None)
+
+    def cache(n_slots=32, h=host, up_s=None, slot_up=FAKE.value, slot_bs=None, slot_of=FAKE.value):
+        return moe.Cache(n_slots, h, up_s, up_s, slot_up, FAKE.value, slot_bs, slot_bs, slot_of)
+
+    def init(c, st=state, nb=n):
+        return lib.moe_cache_init(ctypes.byref(d), ctypes.byref(c), st, nb, None)
+
+    assert init(cache(n_slots=4)) == moe.EINVAL
+    assert init(cache(n_slots=200)) == moe.EINVAL
+    assert init(cache(slot_up=None)) == moe.EINVAL
+    assert init(cache(slot_of=None)) == moe.EINVAL
+    # quantised banks need their resident scales, NVFP4 also block scales
+    assert init(cache(h=moe.Experts(1, FAKE.value, FAKE.value, None, None, None, None))) == moe.EINVAL
+    nv = moe.Experts(2, FAKE.value, FAKE.value, None, None, None, None)
+    assert init(cache(h=nv, up_s=FAKE.value, slot_bs=FAKE.value)) == moe.EINVAL
+    assert init(cache(), st=None) == moe.EINVAL
+    assert init(cache(), nb=n - 1) == moe.EINVAL
+    assert init(cache(), st=ctypes.c_void_p(ctypes.addressof(state) + 4)) == moe.EINVAL
+    # a state moe_cache_init has not set up is refused before any launch
+    c = cache()
+    need = lib.moe_workspace_size(ctypes.byref(d), 0, 4)
+    assert lib.moe_forward_cached(ctypes.byref(d), 4, FAKE, FAKE, FAKE, ctypes.byref(c), state,
+                                  FAKE, 1, FAKE, need, None, None) == moe.EINVAL
+    assert lib.moe_forward_cached(ctypes.byref(d), 4, FAKE, FAKE, FAKE, None, state, FAKE, 1,
+                                  FAKE, need, None, None) == moe.EINVAL
+
+
 def test_quantize_validation(lib):
     d = _dims()
     q = lib.moe_quantize_experts

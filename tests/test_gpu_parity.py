@@ -245,6 +245,77 @@ def test_forward_empty_and_single(full):
     assert torch.isfinite(y).all()
 
 
+# --------------------------------------------------------------------------- expert cache
+class _LruModel:
+    """Independent model of the cache's replacement: touched experts not
+    resident (in increasing id) take the lowest free slot, else the slot of
+    the least recently used resident expert the batch does not touch (ties
+    to the lower slot)."""
+
+    def __init__(self, n_slots):
+        self.n, self.slot, self.last, self.tick = n_slots, {}, {}, 0
+
+    def step(self, touched):
+        self.tick += 1
+        hits = [e for e in sorted(touched) if e in self.slot]
+        misses = [e for e in sorted(touched) if e not in self.slot]
+        for e in hits:
+            self.last[e] = self.tick
+        for e in misses:
+            used = set(self.slot.values())
+            free = [i for i in range(self.n) if i not in used]
+            if free:
+                s = free[0]
+            else:
+                victim = min((r for r in self.slot if r not in touched),
+                             key=lambda r: (self.last[r], self.slot[r]))
+                s = self.slot.pop(victim)
+            self.slot[e] = s
+            self.last[e] = self.tick
+        return len(hits), len(misses)
+
+
+@pytest.mark.parametrize("fmt", ["bf16", "fp8", "nvfp4"])
+def test_forward_cached_equals_resident(full, fmt):
+    # batches of different tokens through a 32-slot cache: every output equals
+    # the resident bank's bit for bit, and hits, misses and uploaded bytes
+    # follow the replacement model (batch 2 repeats batch 0: all hits)
+    bank = full.bank(fmt)
+    cache = moe.ExpertCache(bank, 32)
+    model = _LruModel(32)
+    H, F = FULL.hidden, FULL.ffn
+    per_expert = {"bf16": 4 * H * F, "fp8": 2 * H * F, "nvfp4": H * F + H * F // 8}[fmt]
+    for i, (T, seed) in enumerate([(4, 1), (4, 2), (4, 1), (3, 3), (1, 4), (4, 5), (4, 6)]):
+        x = synth.make_tokens_device(T, FULL, seed=7000 + seed)
+        ids, g = moe.route(x, full.router)
+        y_ref = moe.forward(x, ids, g, bank)
+        y, st = moe.forward_cached(x, ids, g, cache)
+        torch.cuda.synchronize()
+        assert torch.equal(y, y_ref), (fmt, i)
+        touched = set(ids.cpu().numpy().ravel().tolist())
+        hits, misses = model.step(touched)
+        assert (st["touched"], st["hits"], st["misses"]) == (len(touched), hits, misses), (i, st)
+        assert st["bytes_uploaded"] == misses * per_expert
+    _log(f"{fmt}: cached forwards equal the resident bank")
+
+
+def test_forward_cached_rejects_batch_larger_than_cache(full):
+    bank = full.bank("bf16")
+    cache = moe.ExpertCache(bank, 16)
+    x = synth.make_tokens_device(64, FULL, seed=7100)
+    ids, g = moe.route(x, full.router)
+    with pytest.raises(moe.MoeError) as err:
+        moe.forward_cached(x, ids, g, cache)
+    assert err.value.status == moe.EUNSUPPORTED
+    # the cache is still usable, and no slot was given away by the failed call
+    x = synth.make_tokens_device(2, FULL, seed=7101)
+    ids, g = moe.route(x, full.router)
+    y, st = moe.forward_cached(x, ids, g, cache)
+    y_ref = moe.forward(x, ids, g, bank)
+    torch.cuda.synchronize()
+    assert torch.equal(y, y_ref) and st["hits"] == 0
+
+
 # --------------------------------------------------------------------------- end to end
 def test_layer_end_to_end_decode(full):
     T = 64
