@@ -17,6 +17,9 @@ read outside the events, so no step finds the previous step's weights in the
 each step (the same read before each): `step_ms_events` gives the p10 / p50 /
 p90 of those step times.
 
+`--cache-slots N` instead times steps through moe_forward_cached, with the
+expert bank in pinned host memory and N device slots (uploads included).
+
 Prints one JSON line.  `roofline` describes the dominant kernel (algorithmic
 bytes or flops per launch / its mean duration); `cpu_baseline` is the CPU
 oracle timed on this host on a bounded sample of the same workload.
@@ -52,6 +55,10 @@ def parse():
                         "(reported beside the eager headline)")
     p.add_argument("--copy-calibration", action="store_true",
                    help="only run a plain 1 GiB device copy (reference for HBM byte counters)")
+    p.add_argument("--cache-slots", type=int, default=0,
+                   help="single-layer workloads: keep the expert bank in pinned host memory and "
+                        "run each step through moe_forward_cached with this many device slots, "
+                        "cycling over 8 token batches (uploads over PCIe are in the timing)")
     return p.parse_args()
 
 
@@ -92,6 +99,71 @@ def weight_bytes_per_expert(fmt, F, H):
     return n // 2 + n // 16 + 4
 
 
+def cached_bench(args, wl):
+    """Steps through moe_forward_cached: the expert bank lives in pinned host
+    memory and `cache_slots` device slots hold the experts the batches select.
+    The step cycles over 8 token batches of the workload's size, so the
+    selected experts change from step to step; its time includes the upload of
+    the missing experts over PCIe and the wait for the routing counts."""
+    import torch
+
+    import sparse_moe_routed_amd as moe
+    from sparse_moe_routed_amd import synth
+
+    T, fmt = wl["T"], wl["fmt"]
+    ld = moe.LayerDims()
+    dev = torch.device("cuda:0")
+    w_r, b = synth.make_router(0)
+    up, down = synth.make_experts(0)
+    bank = moe.quantize_experts(up.to(dev), down.to(dev), fmt, ld)
+    del up, down
+    router = moe.pack_router(w_r.to(dev), b.to(dev), ld)
+    cache = moe.ExpertCache(bank, args.cache_slots, ld)
+    bank.up = bank.down = bank.up_bs = bank.down_bs = None  # the device keeps the slots and scales
+    torch.cuda.empty_cache()
+    xs = [synth.make_tokens_device(T, seed=9000 + i) for i in range(8)]
+    ids = torch.empty((T, ld.top_k), dtype=torch.int32, device=dev)
+    gates = torch.empty((T, ld.top_k), dtype=torch.float32, device=dev)
+    y = torch.empty((T, ld.hidden), dtype=torch.float32, device=dev)
+    ws = moe.workspace(ld, fmt, T, dev)
+    rws = moe.route_workspace(ld, T, dev)
+    totals = {"touched": 0, "hits": 0, "misses": 0, "bytes_uploaded": 0}
+
+    def step(i, count):
+        x = xs[i % len(xs)]
+        moe.route(x, router, ld, ids=ids, gates=gates, ws=rws)
+        _, st = moe.forward_cached(x, ids, gates, cache, ld, ws=ws, y=y)
+        if count:
+            for k in totals:
+                totals[k] += st[k]
+
+    for i in range(args.warmup):
+        step(i, False)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(args.warmup + i, True)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    out = {
+        "metric": "MoE-layer tokens/s with the expert bank in host memory (1 GPU)",
+        "value": round(T * args.steps / wall, 1), "unit": "tokens/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(wall * 1e3 / args.steps, 4), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": fmt,
+        "data": "synthetic (seeded; 8 token batches in turn)",
+        "config": {"workload": args.workload, "T": T, "format": fmt,
+                   "cache_slots": args.cache_slots, "batches": len(xs)},
+        "cache": {"touched_per_step": round(totals["touched"] / args.steps, 2),
+                  "hit_rate": round(totals["hits"] / max(1, totals["touched"]), 4),
+                  "misses_per_step": round(totals["misses"] / args.steps, 2),
+                  "uploaded_mb_per_step": round(totals["bytes_uploaded"] / args.steps / 1e6, 2),
+                  "upload_gbs": round(totals["bytes_uploaded"] / wall / 1e9, 2)},
+        "roofline": None,
+    }
+    print(json.dumps(out), flush=True)
+
+
 def main():
     args = parse()
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -122,6 +194,10 @@ def main():
         sys.exit(f"unknown workload {args.workload}; choose from {sorted(synth.WORKLOADS)}")
     wl = synth.WORKLOADS[args.workload]
     T, fmt, n_layers = wl["T"], wl["fmt"], wl["layers"]
+    if args.cache_slots:
+        if n_layers != 1:
+            sys.exit("--cache-slots applies to single-layer workloads")
+        return cached_bench(args, wl)
     dims = synth.Dims()
     ld = moe.LayerDims()
     H, F, E, k = dims.hidden, dims.ffn, dims.n_experts, dims.top_k

@@ -233,8 +233,9 @@ int32_t moe_cache_init(const moe_dims* dims, const moe_cache* cache, void* state
  * experts, updates slot_of and runs the expert GEMMs on the slots; y equals
  * moe_forward's on the same bank bit for bit.  If the batch selects more
  * experts than there are slots it returns MOE_EUNSUPPORTED after the
- * permutation, with nothing uploaded and y not written.  Not capturable in a
- * HIP graph (it waits for the stream).  stats [host] may be NULL. */
+ * permutation, with nothing uploaded and y not written.  After MOE_EHIP the
+ * cache must be set up again with moe_cache_init.  Not capturable in a HIP
+ * graph (it waits for the stream).  stats [host] may be NULL. */
 int32_t moe_forward_cached(const moe_dims* dims, int32_t T, const void* x,
                            const int32_t* ids, const float* gates, const moe_cache* cache,
                            void* state, void* y, int32_t y_dtype, void* ws, size_t ws_bytes,

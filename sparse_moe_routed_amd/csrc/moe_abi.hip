@@ -413,8 +413,9 @@ int32_t forward_impl(const moe_dims* dims, int32_t T, const void* x, const int32
       if (ce != hipSuccess) return MOE_EHIP;
       bytes += static_cast<int64_t>(up_b + down_b + up_sb + down_sb);
     }
-    if (hipMemcpyAsync(c->slot_of, v.slot_of, static_cast<size_t>(E) * 4, hipMemcpyHostToDevice,
-                       st) != hipSuccess)
+    // the device map changes only with an upload (moe_cache_init wrote it first)
+    if (misses > 0 && hipMemcpyAsync(c->slot_of, v.slot_of, static_cast<size_t>(E) * 4,
+                                     hipMemcpyHostToDevice, st) != hipSuccess)
       return MOE_EHIP;
     w_slot = c->slot_of;
     if (cc->stats) *cc->stats = moe_cache_stats{touched, hits, misses, bytes};
