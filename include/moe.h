@@ -196,7 +196,8 @@ int32_t moe_forward_timed(const moe_dims* dims, int32_t T, const void* x,
  *   slot_up_bs, slot_down_bs  [dev] NVFP4 block scales of the slots
  *   slot_of   [dev] int32 [E]: the slot of each expert, written by the library
  *   state     [host] moe_cache_state_size bytes of replacement state,
- *             8-byte aligned, kept by the caller between calls */
+ *             8-byte aligned, kept by the caller between calls
+ * Calls that share a cache (its slots, map or state) must not overlap. */
 typedef struct {
   int32_t n_slots;
   moe_experts host;
