@@ -299,6 +299,26 @@ def test_forward_cached_equals_resident(full, fmt):
     _log(f"{fmt}: cached forwards equal the resident bank")
 
 
+@pytest.mark.parametrize("fmt", ["bf16", "fp8", "nvfp4"])
+def test_forward_cached_prefill_tiles(full, fmt):
+    # a small batch first, so that the 600-token batch (prefill tiles) finds
+    # some experts resident and places the rest in later slots: the slot map
+    # is not the identity when the prefill kernels read through it
+    bank = full.bank(fmt)
+    cache = moe.ExpertCache(bank, FULL.n_experts)
+    for T, seed in ((4, 11), (600, 12)):
+        x = synth.make_tokens_device(T, FULL, seed=7200 + seed)
+        ids, g = moe.route(x, full.router)
+        y_ref = moe.forward(x, ids, g, bank)
+        y, st = moe.forward_cached(x, ids, g, cache)
+        torch.cuda.synchronize()
+        assert torch.equal(y, y_ref), (fmt, T)
+    slot_of = cache.slot_of.cpu().numpy()
+    live = slot_of[slot_of >= 0]
+    assert live.size >= st["touched"] and np.unique(live).size == live.size  # distinct slots
+    assert not np.array_equal(slot_of, np.arange(FULL.n_experts))
+
+
 def test_forward_cached_rejects_batch_larger_than_cache(full):
     bank = full.bank("bf16")
     cache = moe.ExpertCache(bank, 16)
