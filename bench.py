@@ -11,7 +11,8 @@ layers with pre-norm and residual.  Inputs are resident in HBM before timing.
 W untimed warm-up steps, then exactly K steps between two device
 synchronisations, with no events.  Per-stage durations come from a second
 pass of K steps with HIP events recorded at every stage boundary on the
-stream the kernels run on; before each of those steps a 512 MB buffer is
+stream the kernels run on, plus events stamped with the two GEMM kernels' own
+start and end (hipExtLaunchKernel); before each of those steps a 512 MB buffer is
 read outside the events, so no step finds the previous step's weights in the
 256 MB Infinity Cache.  A third pass records one event before and one after
 each step (the same read before each): `step_ms_events` gives the p10 / p50 /
@@ -21,7 +22,8 @@ p90 of those step times.
 expert bank in pinned host memory and N device slots (uploads included).
 
 Prints one JSON line.  `roofline` describes the dominant kernel (algorithmic
-bytes or flops per launch / its mean duration); `cpu_baseline` is the CPU
+bytes or flops per launch / the mean of its kernel's own start-to-end
+durations in the second pass); `cpu_baseline` is the CPU
 oracle timed on this host on a bounded sample of the same workload.
 """
 from __future__ import annotations
@@ -228,7 +230,7 @@ def main():
     xs = x0.clone()
     torch.cuda.synchronize()
     stream = torch.cuda.current_stream().cuda_stream
-    n_ev = moe.N_STAGES + 1
+    n_ev = moe.N_TIMED_EVENTS
 
     def run_layer(L, x_in, ev=None):
         """route + forward of one layer; ev = (route events, stage events) or None"""
@@ -272,7 +274,9 @@ def main():
 
     # pass 2 (attribution): K more steps with HIP events at every stage
     # boundary, recorded on the stream the kernels run on (events add a few
-    # microseconds per step, so pass 1 alone gives the headline)
+    # microseconds per step, so pass 1 alone gives the headline), and on the
+    # two GEMM launches themselves: hipExtLaunchKernel stamps those events
+    # with the kernel's own start and end, the interval a kernel trace reports
     # (stacked workloads: events around every layer, averaged over the layers)
     timed_stages = True
     stage_ms = {}
@@ -292,6 +296,10 @@ def main():
     stage_ms["route"] = float(np.mean([hip.elapsed(er[0], er[1]) for er, _ in flat]))
     for si, name in enumerate(moe.STAGES):
         stage_ms[name] = float(np.mean([hip.elapsed(es[si], es[si + 1]) for _, es in flat]))
+    j0 = moe.N_STAGES + 1
+    gemm_kernel_ms = {
+        "up": float(np.mean([hip.elapsed(es[j0], es[j0 + 1]) for _, es in flat])),
+        "down": float(np.mean([hip.elapsed(es[j0 + 2], es[j0 + 3]) for _, es in flat]))}
     for er, es in flat:
         for h in er + es:
             hip.destroy(h)
@@ -350,8 +358,8 @@ def main():
     flops_up = 2.0 * R * F * H
     roof = None
     if timed_stages:
-        dom = "up" if stage_ms["up"] >= stage_ms["down"] else "down"
-        dur_s = stage_ms[dom] * 1e-3
+        dom = "up" if gemm_kernel_ms["up"] >= gemm_kernel_ms["down"] else "down"
+        dur_s = gemm_kernel_ms[dom] * 1e-3
         if T <= 256:
             # weight-streaming launch: bytes of the touched experts' panels plus
             # its activation input and output
@@ -397,6 +405,7 @@ def main():
         "layer_tflops": round(2 * flops_up / (layer_ms * 1e-3) / 1e12, 2),
         "experts_touched": touched,
         "stage_ms": {k2: round(v, 4) for k2, v in stage_ms.items()},
+        "gemm_kernel_ms": {k2: round(v, 4) for k2, v in gemm_kernel_ms.items()},
         "step_ms_events": step_pct,
         "roofline": roof,
     }

@@ -48,7 +48,7 @@
 extern "C" {
 #endif
 
-#define MOE_ABI_VERSION 4
+#define MOE_ABI_VERSION 5
 
 typedef enum {
   MOE_OK = 0,
@@ -166,11 +166,17 @@ int32_t moe_forward(const moe_dims* dims, int32_t T, const void* x,
                     void* ws, size_t ws_bytes, void* stream);
 
 /* moe_forward with stage timing.  `events` [host] holds n_events >= 7
- * hipEvent_t handles created by the caller; events[i] is recorded on `stream`
- * before stage i and events[6] after the last one.  Stages: 0 permutation
- * (histogram, prefix sum, scatter), 1 token quantisation (FP8/NVFP4), 2 up
- * projection + ReLU^2, 3 intermediate quantisation (FP8/NVFP4), 4 down
- * projection, 5 combine.  Results are identical to moe_forward. */
+ * hipEvent_t handles created by the caller (with timing enabled);
+ * events[i] is recorded on `stream` before stage i and events[6] after the
+ * last one.  Stages: 0 permutation (histogram, prefix sum, scatter), 1 token
+ * quantisation (FP8/NVFP4), 2 up projection + ReLU^2, 3 intermediate
+ * quantisation (FP8/NVFP4), 4 down projection, 5 combine.
+ * With n_events >= 11, events[7], events[8] take the start and end of the up
+ * projection kernel itself and events[9], events[10] those of the down
+ * projection kernel (stamped from the kernels' dispatch packets through
+ * hipExtLaunchKernel, so they exclude the marker packets around a stage; a
+ * launch with no tiles records both back to back).  Results are identical
+ * to moe_forward. */
 #define MOE_N_STAGES 6
 int32_t moe_forward_timed(const moe_dims* dims, int32_t T, const void* x,
                           const int32_t* ids, const float* gates,

@@ -113,7 +113,7 @@ _SIGS = {
 }
 
 _lib = None
-ABI_VERSION = 4  # MOE_ABI_VERSION of include/moe.h this binding describes
+ABI_VERSION = 5  # MOE_ABI_VERSION of include/moe.h this binding describes
 
 
 def lib():
@@ -289,13 +289,15 @@ def forward(x: torch.Tensor, ids: torch.Tensor, gates: torch.Tensor, experts: Ex
 
 N_STAGES = 6
 STAGES = ("permute", "quant_x", "up", "quant_act", "down", "combine")
+N_TIMED_EVENTS = N_STAGES + 5
 
 
 def forward_timed(x: torch.Tensor, ids: torch.Tensor, gates: torch.Tensor, experts: ExpertBank,
                   events, dims: LayerDims = LayerDims(), y_dtype: torch.dtype = torch.float32,
                   ws: Optional[torch.Tensor] = None, y: Optional[torch.Tensor] = None) -> torch.Tensor:
     """moe_forward_timed: like forward, recording the caller's hipEvent_t handles
-    (a sequence of N_STAGES + 1 ints) before each stage and after the last."""
+    (a sequence of N_STAGES + 1 ints) before each stage and after the last;
+    N_TIMED_EVENTS handles add the up and down GEMM kernels' own start and end."""
     T = x.shape[0]
     if ws is None:
         ws = workspace(dims, experts.fmt, T, x.device)

@@ -45,6 +45,7 @@
 //          K step of a tile.
 // Epilogues: up writes bf16(relu(h)^2) (and the tensor amax for quantised
 // formats); down writes fp32 gate * h per sorted row.
+#include <hip/hip_ext.h>
 #include <type_traits>
 
 #include "moe_common.h"
@@ -780,26 +781,45 @@ __global__ __launch_bounds__(WM* WN * 64) void grouped_gemm_dma_kernel(GemmArgs 
   if constexpr (STAGE == 0 && FMT != kBF16) block_amax_to_slots(local_max, g.amax);
 }
 
+// One launch of a GEMM kernel over `blocks` workgroups (a multiple of the 8
+// XCDs).  With timing events the launch goes through hipExtLaunchKernel, which
+// stamps them with the kernel's own start and end; a launch with no tiles
+// records both events back to back.
+hipError_t dispatch(const void* kernel, long long blocks, int threads, const GemmArgs& g,
+                    hipStream_t stream, const KernelEvents& ev) {
+  const bool timed = ev.start || ev.stop;
+  if (blocks <= 0) {
+    hipError_t e = hipSuccess;
+    if (ev.start) e = hipEventRecord(ev.start, stream);
+    if (ev.stop && e == hipSuccess) e = hipEventRecord(ev.stop, stream);
+    return e;
+  }
+  GemmArgs a = g;
+  void* args[] = {&a};
+  if (timed)
+    return hipExtLaunchKernel(kernel, dim3(static_cast<unsigned>(blocks)), dim3(threads), args, 0,
+                              stream, ev.start, ev.stop, 0);
+  return hipLaunchKernel(kernel, dim3(static_cast<unsigned>(blocks)), dim3(threads), args, 0,
+                         stream);
+}
+
 template <int FMT, int STAGE, int BM, int BN, int WM, int WN, int NBUF>
-hipError_t launch_dma(const GemmArgs& g, hipStream_t stream) {
+hipError_t launch_dma(const GemmArgs& g, hipStream_t stream, const KernelEvents& ev) {
   const int n_ntiles = (g.N + BN - 1) / BN;
   long long blocks = static_cast<long long>(g.max_tiles) * n_ntiles;
   blocks = (blocks + 7) / 8 * 8;
-  if (blocks <= 0) return hipSuccess;
-  hipLaunchKernelGGL((grouped_gemm_dma_kernel<FMT, STAGE, BM, BN, WM, WN, NBUF>), dim3(blocks),
-                     dim3(WM * WN * 64), 0, stream, g);
-  return hipGetLastError();
+  return dispatch(reinterpret_cast<const void*>(
+                      &grouped_gemm_dma_kernel<FMT, STAGE, BM, BN, WM, WN, NBUF>),
+                  blocks, WM * WN * 64, g, stream, ev);
 }
 
 template <int FMT, int STAGE, int BM, int BN, int WM, int WN>
-hipError_t launch_one(const GemmArgs& g, hipStream_t stream) {
+hipError_t launch_one(const GemmArgs& g, hipStream_t stream, const KernelEvents& ev) {
   const int n_ntiles = (g.N + BN - 1) / BN;
   long long blocks = static_cast<long long>(g.max_tiles) * n_ntiles;
   blocks = (blocks + 7) / 8 * 8;
-  if (blocks <= 0) return hipSuccess;
-  hipLaunchKernelGGL((grouped_gemm_kernel<FMT, STAGE, BM, BN, WM, WN>), dim3(blocks),
-                     dim3(WM * WN * 64), 0, stream, g);
-  return hipGetLastError();
+  return dispatch(reinterpret_cast<const void*>(&grouped_gemm_kernel<FMT, STAGE, BM, BN, WM, WN>),
+                  blocks, WM * WN * 64, g, stream, ev);
 }
 
 
@@ -842,19 +862,20 @@ constexpr int kDecodeBuffers = 3;
 constexpr int kNarrowUpMaxT = 16;
 
 template <int FMT, int STAGE>
-hipError_t launch_fmt_stage(int T, const GemmArgs& g, hipStream_t stream) {
+hipError_t launch_fmt_stage(int T, const GemmArgs& g, hipStream_t stream, const KernelEvents& ev) {
   if constexpr (FMT == kNVFP4 || FMT == kFP8) {
     if (T < kDecodeMaxT)
-      return launch_dma<FMT, STAGE, kDecodeRows, 128, 1, 4, kDecodeBuffers>(g, stream);
+      return launch_dma<FMT, STAGE, kDecodeRows, 128, 1, 4, kDecodeBuffers>(g, stream, ev);
   } else {
     if (STAGE == 0 && T < kNarrowUpMaxT) {
-      if constexpr (FMT == kBF16) return launch_one<FMT, STAGE, kDecodeRows, 32, 1, 1>(g, stream);
-      return launch_one<FMT, STAGE, kDecodeRows, 64, 1, 2>(g, stream);
+      if constexpr (FMT == kBF16)
+        return launch_one<FMT, STAGE, kDecodeRows, 32, 1, 1>(g, stream, ev);
+      return launch_one<FMT, STAGE, kDecodeRows, 64, 1, 2>(g, stream, ev);
     }
-    if (T < kDecodeMaxT) return launch_one<FMT, STAGE, kDecodeRows, 128, 1, 4>(g, stream);
+    if (T < kDecodeMaxT) return launch_one<FMT, STAGE, kDecodeRows, 128, 1, 4>(g, stream, ev);
   }
   using P = PrefillTile<FMT, STAGE>;
-  return launch_dma<FMT, STAGE, P::BM, P::BN, P::WM, P::WN, P::NBUF>(g, stream);
+  return launch_dma<FMT, STAGE, P::BM, P::BN, P::WM, P::WN, P::NBUF>(g, stream, ev);
 }
 
 }  // namespace
@@ -871,14 +892,15 @@ GemmShape gemm_shape(int fmt, int stage, int T) {
   }
 }
 
-hipError_t launch_gemm(int fmt, int stage, int T, const GemmArgs& g, hipStream_t stream) {
+hipError_t launch_gemm(int fmt, int stage, int T, const GemmArgs& g, hipStream_t stream,
+                       const KernelEvents& ev) {
   switch (fmt * 2 + stage) {
-    case kBF16 * 2 + 0: return launch_fmt_stage<kBF16, 0>(T, g, stream);
-    case kBF16 * 2 + 1: return launch_fmt_stage<kBF16, 1>(T, g, stream);
-    case kFP8 * 2 + 0: return launch_fmt_stage<kFP8X, 0>(T, g, stream);
-    case kFP8 * 2 + 1: return launch_fmt_stage<kFP8, 1>(T, g, stream);
-    case kNVFP4 * 2 + 0: return launch_fmt_stage<kNVFP4, 0>(T, g, stream);
-    case kNVFP4 * 2 + 1: return launch_fmt_stage<kNVFP4, 1>(T, g, stream);
+    case kBF16 * 2 + 0: return launch_fmt_stage<kBF16, 0>(T, g, stream, ev);
+    case kBF16 * 2 + 1: return launch_fmt_stage<kBF16, 1>(T, g, stream, ev);
+    case kFP8 * 2 + 0: return launch_fmt_stage<kFP8X, 0>(T, g, stream, ev);
+    case kFP8 * 2 + 1: return launch_fmt_stage<kFP8, 1>(T, g, stream, ev);
+    case kNVFP4 * 2 + 0: return launch_fmt_stage<kNVFP4, 0>(T, g, stream, ev);
+    case kNVFP4 * 2 + 1: return launch_fmt_stage<kNVFP4, 1>(T, g, stream, ev);
     default: return hipErrorInvalidValue;
   }
 }

@@ -276,6 +276,17 @@ struct StageMarks {
   void mark(int i) const {
     if (ev && i < n && ev[i]) (void)hipEventRecord(static_cast<hipEvent_t>(ev[i]), st);
   }
+  // events that take the own start and end of GEMM launch `stage` (0 up,
+  // 1 down), when the caller passed them
+  moe::KernelEvents gemm(int stage) const {
+    moe::KernelEvents k;
+    const int i = MOE_N_STAGES + 1 + 2 * stage;
+    if (ev && n >= MOE_N_STAGES + 5) {
+      k.start = static_cast<hipEvent_t>(ev[i]);
+      k.stop = static_cast<hipEvent_t>(ev[i + 1]);
+    }
+    return k;
+  }
 };
 
 // The forward pass.  With `cc` set, the expert weights come from the cache:
@@ -459,7 +470,7 @@ int32_t forward_impl(const moe_dims* dims, int32_t T, const void* x, const int32
   g.row_gate = nullptr;
   g.amax = amax_a;
   g.w_slot = w_slot;
-  err = moe::launch_gemm(fmt, 0, T, g, st);
+  err = moe::launch_gemm(fmt, 0, T, g, st, marks.gemm(0));
   if (err != hipSuccess) return MOE_EHIP;
 
   // 4. intermediate quantisation (fp8 / nvfp4), rows [0, offsets[E])
@@ -490,7 +501,7 @@ int32_t forward_impl(const moe_dims* dims, int32_t T, const void* x, const int32
   g.out = at<float>(ws, L.out_rows);
   g.row_gate = p.row_gate;
   g.amax = nullptr;
-  err = moe::launch_gemm(fmt, 1, T, g, st);
+  err = moe::launch_gemm(fmt, 1, T, g, st, marks.gemm(1));
   if (err != hipSuccess) return MOE_EHIP;
 
   // 6. combine

@@ -86,7 +86,14 @@ struct GemmShape {
 // permutation's tile lists).
 GemmShape gemm_shape(int fmt, int stage, int T);
 
-hipError_t launch_gemm(int fmt, int stage, int T, const GemmArgs& g, hipStream_t stream);
+// Optional timing of one GEMM launch: events that receive the kernel's own
+// start and end (from its dispatch packet, not markers around it).
+struct KernelEvents {
+  hipEvent_t start = nullptr, stop = nullptr;
+};
+
+hipError_t launch_gemm(int fmt, int stage, int T, const GemmArgs& g, hipStream_t stream,
+                       const KernelEvents& ev = KernelEvents{});
 
 // activation quantisers
 hipError_t launch_amax_bf16(const uint16_t* x, const int32_t* n_rows_dev, int rows, int cols,

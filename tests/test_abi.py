@@ -145,6 +145,13 @@ def test_forward_validation(lib):
     assert call(ws=ctypes.c_void_p(FAKE.value + 16)) == moe.EWORKSPACE
     # T == 0: nothing to do, no workspace needed
     assert call(T=0, ws=None, wsb=0) == moe.OK
+    # the timed variant needs at least one event per stage boundary
+    evs = (ctypes.c_void_p * moe.N_TIMED_EVENTS)()
+    for n, want in ((0, moe.EINVAL), (moe.N_STAGES, moe.EINVAL)):
+        assert lib.moe_forward_timed(ctypes.byref(d), 4, FAKE, FAKE, FAKE, ctypes.byref(ex), FAKE,
+                                     1, FAKE, need, None, evs, n) == want
+    assert lib.moe_forward_timed(ctypes.byref(d), 4, FAKE, FAKE, FAKE, ctypes.byref(ex), FAKE,
+                                 1, FAKE, need, None, None, moe.N_TIMED_EVENTS) == moe.EINVAL
 
 
 def test_cache_validation(lib):

@@ -667,3 +667,64 @@ def test_route_forward_in_hip_graph(full, fmt):
         assert torch.equal(ids, ids_ref), (fmt, i)
         assert torch.equal(y, y_ref), (fmt, i)
     _log(f"{fmt}: {len(inputs) * 2} graph replays equal to eager")
+
+
+# --------------------------------------------------------------------------- stage timing
+class _HipEvents:
+    """hipEventCreate / Record / ElapsedTime / Destroy through ctypes."""
+
+    def __init__(self):
+        import ctypes
+        self.c = ctypes
+        self.lib = ctypes.CDLL("libamdhip64.so")
+        self.lib.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        self.lib.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p,
+                                                 ctypes.c_void_p]
+        self.lib.hipEventDestroy.argtypes = [ctypes.c_void_p]
+
+    def create(self, n):
+        out = []
+        for _ in range(n):
+            e = self.c.c_void_p()
+            assert self.lib.hipEventCreate(self.c.byref(e)) == 0
+            out.append(e.value)
+        return out
+
+    def ms(self, a, b):
+        v = self.c.c_float()
+        assert self.lib.hipEventElapsedTime(self.c.byref(v), self.c.c_void_p(a), self.c.c_void_p(b)) == 0
+        return v.value
+
+    def destroy(self, evs):
+        for e in evs:
+            self.lib.hipEventDestroy(self.c.c_void_p(e))
+
+
+@pytest.mark.parametrize("fmt", ["bf16", "fp8", "nvfp4"])
+def test_forward_timed_equals_forward(full, fmt):
+    # moe_forward_timed, with stage events only and with the GEMM kernels'
+    # own start/end events, gives moe_forward's output bit for bit; each GEMM
+    # kernel's interval is positive and lies inside its stage's bracket.
+    # 4 and 64 tokens run the decode kernels, 600 the prefill kernels.
+    hip = _HipEvents()
+    ld = _ld(FULL)
+    bank = full.bank(fmt)
+    slack = 0.002  # ms
+    for T in (4, 64, 600):
+        _log(f"forward_timed {fmt} T={T}")
+        x = _x(T, FULL).cuda()
+        ids, gates = moe.route(x, full.router, ld)
+        y_ref = moe.forward(x, ids, gates, bank, ld)
+        for n in (moe.N_STAGES + 1, moe.N_TIMED_EVENTS):
+            ev = hip.create(n)
+            y = moe.forward_timed(x, ids, gates, bank, ev, ld)
+            torch.cuda.synchronize()
+            assert torch.equal(y, y_ref), (fmt, T, n)
+            if n == moe.N_TIMED_EVENTS:
+                for st, j in ((2, moe.N_STAGES + 1), (4, moe.N_STAGES + 3)):
+                    kernel = hip.ms(ev[j], ev[j + 1])
+                    stage = hip.ms(ev[st], ev[st + 1])
+                    assert 0 < kernel <= stage + slack, (fmt, T, st, kernel, stage)
+                    assert hip.ms(ev[st], ev[j]) >= -slack, (fmt, T, st)
+                    assert hip.ms(ev[j + 1], ev[st + 1]) >= -slack, (fmt, T, st)
+            hip.destroy(ev)
