@@ -92,12 +92,12 @@ __global__ __launch_bounds__(WM* WN * 64) void grouped_gemm_kernel(GemmArgs g) {
   // NVFP4 and the FP8 down projection (fp8 MFMA) run in
   // grouped_gemm_dma_kernel at every size.
   static_assert(FMT == kBF16 || FMT == kFP8X, "BF16 and expanded FP8 only");
-  // 16-byte source chunks per step: A rows 8 each; B rows 8 (bf16) or 4 (fp8
-  // expanded: 64 codes).  When a tile has fewer chunks than threads,
-  // the extra threads repeat a chunk (same data to the same LDS bytes), which
-  // keeps the loads branch-free.
+  // 16-byte source chunks per step: A rows 8 each, bf16 B rows 8 each (FP8
+  // codes are loaded per pair of steps, below).  When a tile has fewer chunks
+  // than threads, the extra threads repeat a chunk (same data to the same LDS
+  // bytes), which keeps the loads branch-free.
   constexpr int A_TOT = BM * 8;
-  constexpr int B_TOT = (FMT == kFP8X) ? BN * 4 : BN * 8;
+  constexpr int B_TOT = BN * 8;
   constexpr int A_CH = (A_TOT + NT - 1) / NT;
   constexpr int B_CH = (B_TOT + NT - 1) / NT;
   constexpr int ESZ = 2;  // bytes per staged element
@@ -155,16 +155,10 @@ __global__ __launch_bounds__(WM* WN * 64) void grouped_gemm_kernel(GemmArgs g) {
   }
   const uint8_t* b_src[B_CH];
   int b_dst[B_CH];
+  if constexpr (FMT == kBF16) {
 #pragma unroll
-  for (int i = 0; i < B_CH; ++i) {
-    const int c = (tid + i * NT) % B_TOT;
-    if constexpr (FMT == kFP8X) {
-      const int r = c >> 2, q = c & 3;  // 16 codes of the row's 64 per step
-      const int n = min(n0 + r, N - 1);
-      const size_t row = static_cast<size_t>(ew) * N + n;
-      b_src[i] = static_cast<const uint8_t*>(g.b) + row * K + q * 16;
-      b_dst[i] = r * kLds + q * 32;
-    } else {
+    for (int i = 0; i < B_CH; ++i) {
+      const int c = (tid + i * NT) % B_TOT;
       const int r = c >> 3, cc = c & 7;
       const int n = min(n0 + r, N - 1);
       const size_t row = static_cast<size_t>(ew) * N + n;
@@ -172,59 +166,116 @@ __global__ __launch_bounds__(WM* WN * 64) void grouped_gemm_kernel(GemmArgs g) {
       b_dst[i] = r * kLds + cc * 16;
     }
   }
+  // Expanded FP8 codes: one K step is 64 codes, half of a 128-byte line of a
+  // weight row.  Their loads cover pairs of steps so that the 8 lanes of a row
+  // read its whole line in one instruction: lane bit 2, flipped on odd
+  // chunks, picks the half, so each thread holds two chunks of each step.
+  constexpr int B_PCH = (FMT == kFP8X) ? BN * 8 / NT : 2;
+  static_assert(FMT != kFP8X || (BN * 8 % NT == 0 && NT % 8 == 0 && B_PCH % 2 == 0),
+                "fp8 pair chunks");
+  const int h0 = (tid >> 2) & 1;
+  const uint8_t* bp_row[B_PCH];
+  int bp_dst[B_PCH];
+  if constexpr (FMT == kFP8X) {
+#pragma unroll
+    for (int i = 0; i < B_PCH; ++i) {
+      const int c = tid + i * NT;
+      const int r = c >> 3, q = c & 3;
+      const int n = min(n0 + r, N - 1);
+      const size_t row = static_cast<size_t>(ew) * N + n;
+      bp_row[i] = static_cast<const uint8_t*>(g.b) + row * K + q * 16;
+      bp_dst[i] = r * kLds + q * 32;
+    }
+  }
 
   // two register sets: the loads of steps s+1 and s+2 are in flight while
-  // step s is multiplied out of LDS
+  // step s is multiplied out of LDS (FP8 codes: two sets of step pairs)
   u32x4 a_reg[kPrefetch][A_CH];
   u32x4 b_reg[kPrefetch][B_CH];
+  u32x4 bp_reg[2][B_PCH];
 
   // Loads are issued unconditionally (no branches around vector memory ops,
   // so the compiler can wait for exactly the set it needs): steps past the end
   // re-read the last step.  K is a multiple of 64, so bf16 rows hold whole
   // 128-byte steps.
-  auto load = [&](int step_in, auto set_c, auto nt_c) {
+  auto load = [&](int step_in, auto set_c, auto nt_c) __attribute__((always_inline)) {
     constexpr int SET = decltype(set_c)::value;
     constexpr bool NT = decltype(nt_c)::value;
     const int step = min(step_in, n_steps - 1);
     const int kb = step * kStepBytes;
 #pragma unroll
     for (int i = 0; i < A_CH; ++i) a_reg[SET][i] = *reinterpret_cast<const u32x4*>(a_src[i] + kb);
+    if constexpr (FMT == kBF16) {
 #pragma unroll
-    for (int i = 0; i < B_CH; ++i) {
-      if constexpr (FMT == kFP8X) {
-        b_reg[SET][i] = *reinterpret_cast<const u32x4*>(b_src[i] + step * 64);
-      } else if constexpr (NT) {
-        b_reg[SET][i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(b_src[i] + kb));
-      } else {
-        b_reg[SET][i] = *reinterpret_cast<const u32x4*>(b_src[i] + kb);
+      for (int i = 0; i < B_CH; ++i) {
+        if constexpr (NT) {
+          b_reg[SET][i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(b_src[i] + kb));
+        } else {
+          b_reg[SET][i] = *reinterpret_cast<const u32x4*>(b_src[i] + kb);
+        }
       }
     }
   };
 
-  auto store = [&](int buf, auto set_c) {
+  // FP8 codes of K steps 2 pair and 2 pair + 1 into pair set PS (a step past
+  // the end re-reads the last one)
+  auto load_pair = [&](int pair, auto ps_c, auto nt_c) __attribute__((always_inline)) {
+    constexpr int PS = decltype(ps_c)::value;
+    constexpr bool NT = decltype(nt_c)::value;
+#pragma unroll
+    for (int i = 0; i < B_PCH; ++i) {
+      const int step = min(2 * pair + (h0 ^ (i & 1)), n_steps - 1);
+      const u32x4* p = reinterpret_cast<const u32x4*>(bp_row[i] + step * 64);
+      if constexpr (NT) {
+        bp_reg[PS][i] = __builtin_nontemporal_load(p);
+      } else {
+        bp_reg[PS][i] = *p;
+      }
+    }
+  };
+
+  // 16 E4M3 codes -> 16 bf16 (unit scale: exact), 32 bytes at dst
+  auto expand_fp8 = [&](uint8_t* dst_b, const u32x4 v) __attribute__((always_inline)) {
+    uint32_t outw[8];
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      const bf16x2 lo = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(v[w], 1.0f, false);
+      const bf16x2 hi = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(v[w], 1.0f, true);
+      outw[2 * w] = __builtin_bit_cast(uint32_t, lo);
+      outw[2 * w + 1] = __builtin_bit_cast(uint32_t, hi);
+    }
+    u32x4* dst = reinterpret_cast<u32x4*>(dst_b);
+    dst[0] = u32x4{outw[0], outw[1], outw[2], outw[3]};
+    dst[1] = u32x4{outw[4], outw[5], outw[6], outw[7]};
+  };
+
+  // the half HS (0: even step, 1: odd step) of pair set PS into buffer buf
+  auto store_pair = [&](int buf, auto ps_c, auto hs_c) __attribute__((always_inline)) {
+    constexpr int PS = decltype(ps_c)::value;
+    constexpr int HS = decltype(hs_c)::value;
+    uint8_t* B = Bs + buf * BN * kLds;
+    const bool odd = (h0 ^ HS) != 0;  // this thread's chunks 2j + 1 hold that step
+#pragma unroll
+    for (int j = 0; j < B_PCH / 2; ++j) {
+      // select values, not array elements, so the arrays stay in registers
+      const u32x4 e = bp_reg[PS][2 * j], o = bp_reg[PS][2 * j + 1];
+      const int de = bp_dst[2 * j], dodd = bp_dst[2 * j + 1];
+      u32x4 v;
+#pragma unroll
+      for (int w = 0; w < 4; ++w) v[w] = odd ? o[w] : e[w];
+      expand_fp8(B + (odd ? dodd : de), v);
+    }
+  };
+
+  auto store = [&](int buf, auto set_c) __attribute__((always_inline)) {
     constexpr int SET = decltype(set_c)::value;
     uint8_t* A = As + buf * BM * kLds;
     uint8_t* B = Bs + buf * BN * kLds;
 #pragma unroll
     for (int i = 0; i < A_CH; ++i) *reinterpret_cast<u32x4*>(A + a_dst[i]) = a_reg[SET][i];
+    if constexpr (FMT == kBF16) {
 #pragma unroll
-    for (int i = 0; i < B_CH; ++i) {
-      if constexpr (FMT == kFP8X) {
-        // 16 E4M3 codes -> 16 bf16 (unit scale: exact)
-        uint32_t outw[8];
-#pragma unroll
-        for (int w = 0; w < 4; ++w) {
-          const bf16x2 lo = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(b_reg[SET][i][w], 1.0f, false);
-          const bf16x2 hi = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(b_reg[SET][i][w], 1.0f, true);
-          outw[2 * w] = __builtin_bit_cast(uint32_t, lo);
-          outw[2 * w + 1] = __builtin_bit_cast(uint32_t, hi);
-        }
-        u32x4* dst = reinterpret_cast<u32x4*>(B + b_dst[i]);
-        dst[0] = u32x4{outw[0], outw[1], outw[2], outw[3]};
-        dst[1] = u32x4{outw[4], outw[5], outw[6], outw[7]};
-      } else {
-        *reinterpret_cast<u32x4*>(B + b_dst[i]) = b_reg[SET][i];
-      }
+      for (int i = 0; i < B_CH; ++i) *reinterpret_cast<u32x4*>(B + b_dst[i]) = b_reg[SET][i];
     }
   };
 
@@ -257,7 +308,7 @@ __global__ __launch_bounds__(WM* WN * 64) void grouped_gemm_kernel(GemmArgs g) {
   const int lk = lane >> 5;  // which K half of a sub-step this lane supplies
 
   // multiply the first ML row blocks of the wave out of LDS buffer buf
-  auto compute = [&](int buf, auto ml_c) {
+  auto compute = [&](int buf, auto ml_c) __attribute__((always_inline)) {
     constexpr int ML = decltype(ml_c)::value;
     if constexpr (ML > 0) {
       const uint8_t* A = As + buf * BM * kLds;
@@ -265,7 +316,7 @@ __global__ __launch_bounds__(WM* WN * 64) void grouped_gemm_kernel(GemmArgs g) {
       using frag = bf16x8;
       // fragments of sub-step s+1 are read while the MFMAs of sub-step s run
       frag af[2][ML], bfr[2][NB];
-      auto rd = [&](int s, int slot) {
+      auto rd = [&](int s, int slot) __attribute__((always_inline)) {
 #pragma unroll
         for (int i = 0; i < ML; ++i)
           af[slot][i] = *reinterpret_cast<const frag*>(
@@ -295,8 +346,8 @@ __global__ __launch_bounds__(WM* WN * 64) void grouped_gemm_kernel(GemmArgs g) {
   // loads (clamped) but does not compute.
   using S0 = std::integral_constant<int, 0>;
   using S1 = std::integral_constant<int, 1>;
-  auto main_loop = [&](auto ml_c, auto nt_c) {
-    auto iter = [&](int step, auto set_next) {
+  auto main_loop = [&](auto ml_c, auto nt_c) __attribute__((always_inline)) {
+    auto iter = [&](int step, auto set_next) __attribute__((always_inline)) {
       // data of step+1 sits in register set (step+1) % 2 == set_next
       if (step < n_steps) compute(step & 1, ml_c);
       store((step + 1) & 1, set_next);
@@ -313,32 +364,68 @@ __global__ __launch_bounds__(WM* WN * 64) void grouped_gemm_kernel(GemmArgs g) {
       iter(step + 1, S0{});
     }
   };
-  static_assert(MB <= 8, "row blocks per wave");
-  auto run = [&](auto nt_c) {
-    switch (ml) {
-      case 0: main_loop(std::integral_constant<int, 0>{}, nt_c); break;
-      case 1: main_loop(std::integral_constant<int, (MB >= 1 ? 1 : MB)>{}, nt_c); break;
-      case 2: main_loop(std::integral_constant<int, (MB >= 2 ? 2 : MB)>{}, nt_c); break;
-      case 3: main_loop(std::integral_constant<int, (MB >= 3 ? 3 : MB)>{}, nt_c); break;
-      case 4: main_loop(std::integral_constant<int, (MB >= 4 ? 4 : MB)>{}, nt_c); break;
-      case 5: main_loop(std::integral_constant<int, (MB >= 5 ? 5 : MB)>{}, nt_c); break;
-      case 6: main_loop(std::integral_constant<int, (MB >= 6 ? 6 : MB)>{}, nt_c); break;
-      case 7: main_loop(std::integral_constant<int, (MB >= 7 ? 7 : MB)>{}, nt_c); break;
-      default: main_loop(std::integral_constant<int, MB>{}, nt_c); break;
+  // FP8 codes: activations per step as above; codes per pair of steps, two
+  // pair sets, so the loads of a pair are issued three steps before its first
+  // step is stored.  Unrolled by four (A set, pair set and half are
+  // compile-time); the loop stops after the iteration that computes the last
+  // step.
+  using F0 = std::false_type;
+  using T1 = std::true_type;
+  auto main_loop_pairs = [&](auto ml_c, auto nt_c) __attribute__((always_inline)) {
+    // iteration `step` computes step, then stages step + 1: its activations
+    // from set a_next, its codes from pair set ps, half hs
+    auto iter = [&](int step, auto a_next, auto ps, auto hs, auto reload) __attribute__((always_inline)) {
+      if (step < n_steps) compute(step & 1, ml_c);
+      store((step + 1) & 1, a_next);
+      store_pair((step + 1) & 1, ps, hs);
+      load(step + 1 + kPrefetch, a_next, nt_c);
+      // both halves of pair set ps are staged: refill it two pairs ahead
+      if constexpr (decltype(reload)::value) load_pair((step + 1) / 2 + 2, ps, nt_c);
+      __syncthreads();
+    };
+    load(0, S0{}, nt_c);
+    load(1, S1{}, nt_c);
+    load_pair(0, S0{}, nt_c);
+    load_pair(1, S1{}, nt_c);
+    store(0, S0{});
+    store_pair(0, S0{}, S0{});
+    load(2, S0{}, nt_c);
+    __syncthreads();
+    for (int step = 0; step < n_steps; step += 4) {
+      iter(step, S1{}, S0{}, S1{}, T1{});
+      if (step + 1 >= n_steps) break;
+      iter(step + 1, S0{}, S1{}, S0{}, F0{});
+      if (step + 2 >= n_steps) break;
+      iter(step + 2, S1{}, S1{}, S1{}, T1{});
+      if (step + 3 >= n_steps) break;
+      iter(step + 3, S0{}, S0{}, S0{}, F0{});
     }
   };
-  // BF16 weight panels that only this workgroup reads (the expert has one
-  // row tile) stream through with non-temporal loads: 7-8 % faster at 4 to
+  static_assert(MB <= 8, "row blocks per wave");
+  auto run = [&](auto nt_c) __attribute__((always_inline)) {
+    auto go = [&](auto ml_c) __attribute__((always_inline)) {
+      if constexpr (FMT == kFP8X) main_loop_pairs(ml_c, nt_c);
+      else main_loop(ml_c, nt_c);
+    };
+    switch (ml) {
+      case 0: go(std::integral_constant<int, 0>{}); break;
+      case 1: go(std::integral_constant<int, (MB >= 1 ? 1 : MB)>{}); break;
+      case 2: go(std::integral_constant<int, (MB >= 2 ? 2 : MB)>{}); break;
+      case 3: go(std::integral_constant<int, (MB >= 3 ? 3 : MB)>{}); break;
+      case 4: go(std::integral_constant<int, (MB >= 4 ? 4 : MB)>{}); break;
+      case 5: go(std::integral_constant<int, (MB >= 5 ? 5 : MB)>{}); break;
+      case 6: go(std::integral_constant<int, (MB >= 6 ? 6 : MB)>{}); break;
+      case 7: go(std::integral_constant<int, (MB >= 7 ? 7 : MB)>{}); break;
+      default: go(std::integral_constant<int, MB>{}); break;
+    }
+  };
+  // Weight panels that only this workgroup reads (the expert has one row
+  // tile) stream through with non-temporal loads: BF16 7-8 % faster at 4 to
   // 128 tokens.  Panels that sibling row tiles re-read keep ordinary loads,
-  // which leave the lines in L2 for them (non-temporal loads there were 5-10 %
-  // slower at 384 and 511 tokens).  Expanded FP8 codes are read in 64-byte
-  // halves of a line, so their second half must stay in L2: ordinary loads.
-  if constexpr (FMT == kBF16) {
-    if (te == 1) run(std::true_type{});
-    else run(std::false_type{});
-  } else {
-    run(std::false_type{});
-  }
+  // which leave the lines in L2 for them (non-temporal loads there were
+  // 5-10 % slower at 384 and 511 tokens).
+  if (te == 1) run(T1{});
+  else run(F0{});
 
   // ---- epilogue.  32x32 f32 result: lane holds column lane%32 and rows
   // 8*(r/4) + 4*(lane/32) + r%4 for r = 0..15.
