@@ -85,8 +85,16 @@ typedef struct {
 
 /* [host] struct of [dev] expert bank pointers.
  *   BF16 : up  bf16 [E, F, H],  down bf16 [E, H, F]
- *   FP8  : up  u8 E4M3 [E, F, H], down u8 [E, H, F]; up_s/down_s fp32 [E]
- *          (weight = dec(code) * s)
+ *   FP8  : up  u8 E4M3 [E, F, H] row-major; down u8 H*F bytes per expert
+ *          in 128-row panels (below); up_s/down_s fp32 [E]
+ *          (weight = dec(code) * s).  Down panels: the H x F matrix is cut
+ *          into panels of rows_p = min(128, H - 128 p) rows, each stored
+ *          K-step-major in steps of 128 codes (the last step 64 codes when
+ *          F % 128 == 64): code j of row n, step s lies at
+ *            128 p * F + s * rows_p * 128 + (n - 128 p) * sb + j,
+ *          sb = min(128, F - 128 s), p = n / 128, from the expert's base, so
+ *          every step of a row is one aligned 128-byte line (F = 1856 rows
+ *          are 14.5 lines; row-major, half of them would straddle lines).
  *   NVFP4: up  u8 F*H/2 bytes per expert, down u8 H*F/2 (two E2M1 codes per
  *          byte, element 2i in the low nibble); up_bs u8 E4M3 F*H/16 bytes
  *          per expert, down_bs H*F/16 (one per 16-element block along K);

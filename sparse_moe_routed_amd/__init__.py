@@ -398,7 +398,8 @@ def quantize_experts(up: torch.Tensor, down: torch.Tensor, fmt: str,
     dev = up.device
     if fmt == "fp8":
         up_q = torch.empty((E, F, H), dtype=torch.uint8, device=dev)
-        down_q = torch.empty((E, H, F), dtype=torch.uint8, device=dev)
+        # down codes: per-expert byte arrays in the panel layout (moe.h)
+        down_q = torch.empty((E, H * F), dtype=torch.uint8, device=dev)
         up_bs = down_bs = None
     elif fmt == "nvfp4":
         # per-expert byte arrays in the panel layout of moe_experts (moe.h)

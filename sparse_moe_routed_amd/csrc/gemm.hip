@@ -580,28 +580,35 @@ __global__ __launch_bounds__(WM* WN * 64) void grouped_gemm_dma_kernel(GemmArgs 
     a_cof[q] = c * 16;
   }
   constexpr int CPR = RB / 16;  // 16-byte chunks per weight row and step
-  // NVFP4 weights sit in panels stored K-step-major (the tile lies inside one
-  // panel): a step of the tile's rows is contiguous, w_step bytes apart
-  static_assert(FMT != kNVFP4 || kNvPanel % BN == 0, "NVFP4 tiles stay inside one panel");
+  // NVFP4 and FP8 (down projection) weights sit in panels stored
+  // K-step-major (the tile lies inside one panel): a step of the tile's rows
+  // is contiguous, w_step bytes apart.  FP8 steps are whole 128-byte lines;
+  // when K % 128 == 64 the last step holds 64 bytes per row, and its chunks
+  // move by b_tail[q] (chunks past K re-read the row's in-range chunk 64
+  // bytes earlier and are zeroed when the fragments are formed).
+  constexpr bool kPanels = FMT == kNVFP4 || FMT == kFP8;
+  static_assert(!kPanels || kNvPanel % BN == 0, "panel-layout tiles stay inside one panel");
+  static_assert(FMT != kFP8 || RB == kFp8StepK, "fp8 panel steps");
   const int nv_pn0 = n0 - n0 % kNvPanel;
   const int nv_rows = nv_panel_rows(N, nv_pn0 / kNvPanel);
-  const int w_step = (FMT == kNVFP4) ? nv_rows * RB : RB;
+  const int w_step = kPanels ? nv_rows * RB : RB;
+  const bool fp8_tail_step = FMT == kFP8 && (K % RB) != 0;
   const uint8_t* b_src[QB];
-  int b_dst[QB], b_cof[QB];
+  int b_dst[QB], b_tail[QB];
 #pragma unroll
   for (int q = 0; q < QB; ++q) {
     const int qi = (wave + q * NW) % NBL;
     const int r = qi * (1024 / RB) + lane / CPR;
     const int c = (lane % CPR) ^ lds_swz<RB>(r);
     const int n = min(n0 + r, N - 1);
-    if constexpr (FMT == kNVFP4) {
+    if constexpr (kPanels) {
       b_src[q] = static_cast<const uint8_t*>(g.b) + (static_cast<size_t>(ew) * N + nv_pn0) * w_bytes +
                  (n - nv_pn0) * RB + c * 16;
     } else {
       b_src[q] = static_cast<const uint8_t*>(g.b) + (static_cast<size_t>(ew) * N + n) * w_bytes + c * 16;
     }
     b_dst[q] = B_OFF + qi * 1024;
-    b_cof[q] = c * 16;
+    b_tail[q] = -((n - nv_pn0) * (RB / 2) + (c & (CPR / 2)) * 16);
   }
   const uint8_t* s_src[QS > 0 ? QS : 1];
   int s_dst[QS > 0 ? QS : 1];
@@ -630,10 +637,11 @@ __global__ __launch_bounds__(WM* WN * 64) void grouped_gemm_dma_kernel(GemmArgs 
                                        16, 0, 0);
     }
     const int wb = step * w_step;              // weight bytes before this step
+    const bool tail = fp8_tail_step && step == n_steps - 1;
 #pragma unroll
     for (int q = 0; q < QB; ++q) {
       const uint8_t* p = b_src[q] + wb;
-      if constexpr (FMT == kFP8) p = (wb + b_cof[q] >= w_bytes) ? p - 64 : p;
+      if constexpr (FMT == kFP8) p = tail ? p + b_tail[q] : p;
       __builtin_amdgcn_global_load_lds(p, (__attribute__((address_space(3))) void*)(buf + b_dst[q]),
                                        16, 0, 0);
     }

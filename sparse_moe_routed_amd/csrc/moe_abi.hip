@@ -550,10 +550,10 @@ int32_t moe_quantize_experts(const moe_dims* dims, int32_t fmt, const void* up_b
   const hipStream_t st = static_cast<hipStream_t>(stream);
   const int H = dims->hidden, F = dims->ffn, E = dims->n_experts;
   hipError_t err = moe::launch_quant_weights(fmt, static_cast<const uint16_t*>(up_bf16), E, F, H,
-                                             static_cast<uint8_t*>(up_q), up_bs, up_s, st);
+                                             static_cast<uint8_t*>(up_q), up_bs, up_s, 0, st);
   if (err == hipSuccess)
     err = moe::launch_quant_weights(fmt, static_cast<const uint16_t*>(down_bf16), E, H, F,
-                                    static_cast<uint8_t*>(down_q), down_bs, down_s, st);
+                                    static_cast<uint8_t*>(down_q), down_bs, down_s, 1, st);
   return hip_status(err);
 }
 

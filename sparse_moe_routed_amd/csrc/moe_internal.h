@@ -22,6 +22,11 @@ constexpr int kChunk = 2048;  // flat (token, slot) entries per permutation chun
 // columns inside one panel then reads one contiguous block per K step.
 constexpr int kNvPanel = 128;
 constexpr int kNvStepK = 64;
+// FP8 down-projection codes use the same 128-row panels, K-step-major in
+// steps of kFp8StepK codes (one 128-byte line per row; a last step of 64
+// codes when K % 128 == 64).  Rows of F = 1856 codes are not a whole number
+// of lines, so in row-major order half the rows would straddle lines.
+constexpr int kFp8StepK = 128;
 
 __host__ __device__ __forceinline__ int nv_panel_rows(int N, int p) {
   const int left = N - p * kNvPanel;
@@ -114,8 +119,10 @@ hipError_t launch_zero_u32(uint32_t* p, int n, hipStream_t stream);
 hipError_t launch_combine(const float* rows, const int32_t* inv, int T, int k, int H, void* y,
                           int y_f32, hipStream_t stream);
 
+// fp8_panels: write FP8 codes in the panel layout (down projection) rather
+// than row-major (up projection)
 hipError_t launch_quant_weights(int fmt, const uint16_t* w, int E, int N, int K, uint8_t* q,
-                                uint8_t* bs, float* s, hipStream_t stream);
+                                uint8_t* bs, float* s, int fp8_panels, hipStream_t stream);
 
 hipError_t launch_prenorm(const uint16_t* x, int T, int H, uint16_t* out, hipStream_t stream);
 hipError_t launch_residual(uint16_t* x, const float* y, int T, int H, hipStream_t stream);

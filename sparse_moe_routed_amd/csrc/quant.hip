@@ -170,7 +170,7 @@ __global__ __launch_bounds__(kQThreads) void weight_amax_kernel(const uint16_t* 
 
 __global__ __launch_bounds__(kQThreads) void weight_codes_kernel(
     int fmt, const uint16_t* __restrict__ w, int N, int K, const uint32_t* amax,
-    uint8_t* __restrict__ q, uint8_t* __restrict__ bs) {
+    uint8_t* __restrict__ q, uint8_t* __restrict__ bs, int fp8_panels) {
   const size_t per_expert = static_cast<size_t>(N) * K;
   const int e = blockIdx.y;
   const float a = __uint_as_float(amax[e]);
@@ -197,7 +197,20 @@ __global__ __launch_bounds__(kQThreads) void weight_codes_kernel(
         }
         out[ww] = c[0] | (c[1] << 8) | (c[2] << 16) | (c[3] << 24);
       }
-      reinterpret_cast<u32x4*>(qe)[i] = u32x4{out[0], out[1], out[2], out[3]};
+      // chunk i = 16 codes of row n; row-major, or in the panel layout (rows
+      // of a panel contiguous per K step of up to 128 codes)
+      size_t at = i * 16;
+      if (fp8_panels) {
+        const size_t n = i / static_cast<size_t>(K / 16);
+        const int b = static_cast<int>(i - n * static_cast<size_t>(K / 16));
+        const int p = static_cast<int>(n / kNvPanel), pr = static_cast<int>(n % kNvPanel);
+        const int rows_p = nv_panel_rows(N, p);
+        const int st = b / (kFp8StepK / 16), bq = b % (kFp8StepK / 16);
+        const int step_bytes = min(kFp8StepK, K - st * kFp8StepK);
+        at = static_cast<size_t>(p) * kNvPanel * K + static_cast<size_t>(st) * rows_p * kFp8StepK +
+             static_cast<size_t>(pr) * step_bytes + bq * 16;
+      }
+      *reinterpret_cast<u32x4*>(qe + at) = u32x4{out[0], out[1], out[2], out[3]};
     }
   } else {
     const float S = a > 0.f ? __fdiv_rn(a, 2688.f) : 0.f;
@@ -302,7 +315,7 @@ hipError_t launch_quant_nvfp4(const uint16_t* x, const int32_t* n_rows_dev, int 
 }
 
 hipError_t launch_quant_weights(int fmt, const uint16_t* w, int E, int N, int K, uint8_t* q,
-                                uint8_t* bs, float* s, hipStream_t stream) {
+                                uint8_t* bs, float* s, int fp8_panels, hipStream_t stream) {
   const size_t per = static_cast<size_t>(N) * K;
   hipError_t err = launch_zero_u32(reinterpret_cast<uint32_t*>(s), E, stream);
   if (err != hipSuccess) return err;
@@ -311,7 +324,7 @@ hipError_t launch_quant_weights(int fmt, const uint16_t* w, int E, int N, int K,
                      reinterpret_cast<uint32_t*>(s));
   const int gq = grid_for(per / 16, 64);
   hipLaunchKernelGGL(weight_codes_kernel, dim3(gq, E), dim3(kQThreads), 0, stream, fmt, w, N, K,
-                     reinterpret_cast<const uint32_t*>(s), q, bs);
+                     reinterpret_cast<const uint32_t*>(s), q, bs, fp8_panels);
   hipLaunchKernelGGL(weight_scales_kernel, dim3((E + 255) / 256), dim3(256), 0, stream, fmt, E,
                      s);
   return hipGetLastError();

@@ -463,6 +463,42 @@ def _panels_to_rows(buf: np.ndarray, N: int, K: int, row_step_bytes: int) -> np.
     return out
 
 
+def _fp8_panels_to_rows(buf: np.ndarray, N: int, K: int) -> np.ndarray:
+    """Row-major [N, K] view of one expert's FP8 down-projection codes in the
+    panel layout of moe_experts: 128-row panels, each K-step-major in steps of
+    128 codes, the last step 64 codes when K % 128 == 64."""
+    out = np.empty((N, K), np.uint8)
+    for p0 in range(0, N, 128):
+        rows = min(128, N - p0)
+        at = p0 * K
+        for k0 in range(0, K, 128):
+            sb = min(128, K - k0)
+            out[p0:p0 + rows, k0:k0 + sb] = buf[at:at + rows * sb].reshape(rows, sb)
+            at += rows * sb
+    return out
+
+
+def test_fp8_panel_view_matches_the_abi_formula():
+    # _fp8_panels_to_rows against the byte formula of moe_experts, element by
+    # element, with a short last panel and a 64-code last step
+    N, K = 200, 192
+    rows = np.random.default_rng(5).integers(0, 256, (N, K), dtype=np.uint8)
+    buf = np.full(N * K, 0, np.uint8)
+    seen = np.zeros(N * K, bool)
+    for n in range(N):
+        p = n // 128
+        rows_p = min(128, N - 128 * p)
+        for k in range(K):
+            st, j = divmod(k, 128)
+            sb = min(128, K - 128 * st)
+            at = 128 * p * K + st * rows_p * 128 + (n - 128 * p) * sb + j
+            assert not seen[at]
+            seen[at] = True
+            buf[at] = rows[n, k]
+    assert seen.all()
+    assert np.array_equal(_fp8_panels_to_rows(buf, N, K), rows)
+
+
 @pytest.mark.parametrize("fmt", ["fp8", "nvfp4"])
 def test_weight_codes_bit_exact(full, fmt):
     bank = full.bank(fmt)
@@ -475,6 +511,8 @@ def test_weight_codes_bit_exact(full, fmt):
             s_gpu = getattr(bank, name + "_s")[e].item()
             if fmt == "fp8":
                 q, s = codecs.fp8_quantize(wf)
+                if name == "down":
+                    q_gpu = _fp8_panels_to_rows(q_gpu.reshape(-1), N, K)
                 assert np.array_equal(q_gpu, q), (name, e)
             else:
                 q, sb, s = codecs.nvfp4_quantize(wf)
