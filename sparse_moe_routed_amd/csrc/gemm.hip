@@ -626,7 +626,10 @@ __global__ __launch_bounds__(WM* WN * 64) void grouped_gemm_dma_kernel(GemmArgs 
   // re-read the last step (that buffer is not read again); a chunk past the
   // FP8 K tail reads the in-range chunk 64 bytes earlier and is zeroed when
   // the fragments are formed.
-  auto dma = [&](int step_in, uint8_t* buf) {
+  auto dma = [&](int step_in, uint8_t* buf, auto nt_c) {
+    // weight loads carry the non-temporal cache-policy bit (aux bit 1) when
+    // no other workgroup reads this weight panel
+    constexpr int kWeightPolicy = decltype(nt_c)::value ? 2 : 0;
     const int step = min(step_in, n_steps - 1);
     const int kb = step * 128;                 // activation bytes before this step
 #pragma unroll
@@ -643,7 +646,7 @@ __global__ __launch_bounds__(WM* WN * 64) void grouped_gemm_dma_kernel(GemmArgs 
       const uint8_t* p = b_src[q] + wb;
       if constexpr (FMT == kFP8) p = tail ? p + b_tail[q] : p;
       __builtin_amdgcn_global_load_lds(p, (__attribute__((address_space(3))) void*)(buf + b_dst[q]),
-                                       16, 0, 0);
+                                       16, 0, kWeightPolicy);
     }
     if constexpr (QS > 0) {
 #pragma unroll
@@ -810,45 +813,58 @@ __global__ __launch_bounds__(WM* WN * 64) void grouped_gemm_dma_kernel(GemmArgs 
 
   // one K step: wait for this wave's loads of the step, meet, start the loads
   // NBUF - 1 steps ahead into the buffer everyone finished reading, multiply
-  auto body = [&](int step, const uint8_t* cur, uint8_t* ahead, auto ml_c) {
+  auto body = [&](int step, const uint8_t* cur, uint8_t* ahead, auto ml_c, auto nt_c) {
     __builtin_amdgcn_s_waitcnt(vmcnt_imm((NBUF - 2) * DPS));
     __asm__ volatile("s_barrier" ::: "memory");
-    dma(step + NBUF - 1, ahead);
+    dma(step + NBUF - 1, ahead, nt_c);
     if (step < n_steps) compute(cur, step, ml_c);
   };
-  auto main_loop = [&](auto ml_c) {
-    dma(0, lds0);
+  auto main_loop = [&](auto ml_c, auto nt_c) {
+    dma(0, lds0, nt_c);
     if constexpr (NBUF == 4) {
-      dma(1, lds1);
-      dma(2, lds2);
+      dma(1, lds1, nt_c);
+      dma(2, lds2, nt_c);
       for (int step = 0; step < n_steps; step += 4) {
-        body(step, lds0, lds3, ml_c);
-        body(step + 1, lds1, lds0, ml_c);
-        body(step + 2, lds2, lds1, ml_c);
-        body(step + 3, lds3, lds2, ml_c);
+        body(step, lds0, lds3, ml_c, nt_c);
+        body(step + 1, lds1, lds0, ml_c, nt_c);
+        body(step + 2, lds2, lds1, ml_c, nt_c);
+        body(step + 3, lds3, lds2, ml_c, nt_c);
       }
     } else if constexpr (NBUF == 3) {
-      dma(1, lds1);
+      dma(1, lds1, nt_c);
       for (int step = 0; step < n_steps; step += 3) {
-        body(step, lds0, lds2, ml_c);
-        body(step + 1, lds1, lds0, ml_c);
-        body(step + 2, lds2, lds1, ml_c);
+        body(step, lds0, lds2, ml_c, nt_c);
+        body(step + 1, lds1, lds0, ml_c, nt_c);
+        body(step + 2, lds2, lds1, ml_c, nt_c);
       }
     } else {
       for (int step = 0; step < n_steps; step += 2) {
-        body(step, lds0, lds1, ml_c);
-        body(step + 1, lds1, lds0, ml_c);
+        body(step, lds0, lds1, ml_c, nt_c);
+        body(step + 1, lds1, lds0, ml_c, nt_c);
       }
     }
     __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
   };
   static_assert(MB <= 4, "row blocks per wave");
-  switch (ml) {
-    case 0: main_loop(std::integral_constant<int, 0>{}); break;
-    case 1: main_loop(std::integral_constant<int, (MB >= 1 ? 1 : MB)>{}); break;
-    case 2: main_loop(std::integral_constant<int, (MB >= 2 ? 2 : MB)>{}); break;
-    case 3: main_loop(std::integral_constant<int, (MB >= 3 ? 3 : MB)>{}); break;
-    default: main_loop(std::integral_constant<int, MB>{}); break;
+  auto run = [&](auto nt_c) {
+    switch (ml) {
+      case 0: main_loop(std::integral_constant<int, 0>{}, nt_c); break;
+      case 1: main_loop(std::integral_constant<int, (MB >= 1 ? 1 : MB)>{}, nt_c); break;
+      case 2: main_loop(std::integral_constant<int, (MB >= 2 ? 2 : MB)>{}, nt_c); break;
+      case 3: main_loop(std::integral_constant<int, (MB >= 3 ? 3 : MB)>{}, nt_c); break;
+      default: main_loop(std::integral_constant<int, MB>{}, nt_c); break;
+    }
+  };
+  // decode tiles: non-temporal weight loads when this workgroup is the
+  // panel's only reader (the expert has one row tile), as in
+  // grouped_gemm_kernel.  Prefill tiles keep one code path (a second one
+  // costs registers: 132 VGPRs for the FP8 up tile, over the 128 that two
+  // workgroups per CU allow).
+  if constexpr (BM <= 32) {
+    if (te == 1) run(std::true_type{});
+    else run(std::false_type{});
+  } else {
+    run(std::false_type{});
   }
 
   // ---- epilogue (as in grouped_gemm_kernel)
