@@ -184,7 +184,7 @@ int32_t moe_forward(const moe_dims* dims, int32_t T, const void* x,
  * projection kernel (stamped from the kernels' dispatch packets through
  * hipExtLaunchKernel, so they exclude the marker packets around a stage; a
  * launch with no tiles records both back to back).  Results are identical
- * to moe_forward. */
+ * to moe_forward.  With T = 0 nothing is enqueued and no event is recorded. */
 #define MOE_N_STAGES 6
 int32_t moe_forward_timed(const moe_dims* dims, int32_t T, const void* x,
                           const int32_t* ids, const float* gates,
