@@ -310,7 +310,9 @@ int32_t moe_quantize_activation(int32_t fmt, int32_t rows, int32_t cols,
  *                          into out, in one pass (bit-identical to the two
  *                          calls; for the step between stacked layers)
  * x, out [dev] bf16 [T, H] (out must not be x); y [dev] fp32 [T, H];
- * H % 64 == 0.  Row sums of squares are accumulated in double. */
+ * H % 64 == 0; moe_prenorm and moe_residual_prenorm need 16-byte aligned
+ * x, y and out (MOE_EINVAL otherwise).  Row sums of squares are
+ * accumulated in double. */
 int32_t moe_prenorm(int32_t T, int32_t H, const void* x, void* out, void* stream);
 int32_t moe_residual_add(int32_t T, int32_t H, void* x, const float* y, void* stream);
 int32_t moe_residual_prenorm(int32_t T, int32_t H, void* x, const float* y, void* out,

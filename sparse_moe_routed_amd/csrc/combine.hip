@@ -49,16 +49,12 @@ __global__ __launch_bounds__(kCThreads) void combine_kernel(const float* __restr
 }
 
 // out = bf16(x / sqrt(mean(x^2) + 1e-6)), evaluated in double and rounded once
-__global__ __launch_bounds__(kCThreads) void prenorm_kernel(const uint16_t* __restrict__ x, int H,
-                                                            uint16_t* __restrict__ out) {
-  __shared__ double part[kCThreads / 64];
-  const int t = blockIdx.x;
-  const uint16_t* xr = x + static_cast<size_t>(t) * H;
-  double ss = 0.0;
-  for (int c = threadIdx.x; c < H; c += kCThreads) {
-    const double v = bf16_to_f32(xr[c]);
-    ss += v * v;
-  }
+// Pre-norm of one token per workgroup.  Thread i handles the 8-element
+// chunks i, i + kCThreads, ... of the row (16-byte loads and stores); its
+// float64 sum of squares runs over its chunks in order, then across the
+// wave and the waves.  residual_prenorm_kernel uses the same order, so the
+// two give identical results.
+__device__ __forceinline__ double block_sum_f64(double ss, double* part) {
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) ss += __shfl_xor(ss, o);
   if ((threadIdx.x & 63) == 0) part[threadIdx.x >> 6] = ss;
@@ -66,13 +62,44 @@ __global__ __launch_bounds__(kCThreads) void prenorm_kernel(const uint16_t* __re
   double tot = 0.0;
 #pragma unroll
   for (int w = 0; w < kCThreads / 64; ++w) tot += part[w];
-  const double d = sqrt(tot / static_cast<double>(H) + 1e-6);
-  uint16_t* o = out + static_cast<size_t>(t) * H;
-  for (int c = threadIdx.x; c < H; c += kCThreads)
-    o[c] = f64_to_bf16(static_cast<double>(bf16_to_f32(xr[c])) / d);
+  return tot;
 }
 
-// x = bf16(x + y): the sum is exact in double, rounded once
+__device__ __forceinline__ double sum_sq8(const u32x4 v) {
+  double ss = 0.0;
+#pragma unroll
+  for (int w = 0; w < 4; ++w) {
+    const double lo = bf16_to_f32(v[w] & 0xffffu), hi = bf16_to_f32(v[w] >> 16);
+    ss += lo * lo;
+    ss += hi * hi;
+  }
+  return ss;
+}
+
+// out chunk = bf16(x / d) for the 8 values of v
+__device__ __forceinline__ u32x4 scale8(const u32x4 v, double d) {
+  u32x4 o;
+#pragma unroll
+  for (int w = 0; w < 4; ++w) {
+    const uint32_t lo = f64_to_bf16(static_cast<double>(bf16_to_f32(v[w] & 0xffffu)) / d);
+    const uint32_t hi = f64_to_bf16(static_cast<double>(bf16_to_f32(v[w] >> 16)) / d);
+    o[w] = lo | (hi << 16);
+  }
+  return o;
+}
+
+__global__ __launch_bounds__(kCThreads) void prenorm_kernel(const uint16_t* __restrict__ x, int H,
+                                                            uint16_t* __restrict__ out) {
+  __shared__ double part[kCThreads / 64];
+  const int h8 = H / 8;
+  const u32x4* xr = reinterpret_cast<const u32x4*>(x + static_cast<size_t>(blockIdx.x) * H);
+  double ss = 0.0;
+  for (int c = threadIdx.x; c < h8; c += kCThreads) ss += sum_sq8(xr[c]);
+  const double d = sqrt(block_sum_f64(ss, part) / static_cast<double>(H) + 1e-6);
+  u32x4* o = reinterpret_cast<u32x4*>(out + static_cast<size_t>(blockIdx.x) * H);
+  for (int c = threadIdx.x; c < h8; c += kCThreads) o[c] = scale8(xr[c], d);
+}
+
 __global__ __launch_bounds__(kCThreads) void residual_kernel(uint16_t* __restrict__ x,
                                                              const float* __restrict__ y,
                                                              size_t n) {
@@ -89,27 +116,30 @@ __global__ __launch_bounds__(kCThreads) void residual_prenorm_kernel(uint16_t* _
                                                                      int H,
                                                                      uint16_t* __restrict__ out) {
   __shared__ double part[kCThreads / 64];
-  const int t = blockIdx.x;
-  uint16_t* xr = x + static_cast<size_t>(t) * H;
-  const float* yr = y + static_cast<size_t>(t) * H;
+  const int h8 = H / 8;
+  u32x4* xr = reinterpret_cast<u32x4*>(x + static_cast<size_t>(blockIdx.x) * H);
+  const f32x4* yr = reinterpret_cast<const f32x4*>(y + static_cast<size_t>(blockIdx.x) * H);
   double ss = 0.0;
-  for (int c = threadIdx.x; c < H; c += kCThreads) {
-    const uint16_t xn = f64_to_bf16(static_cast<double>(bf16_to_f32(xr[c])) + static_cast<double>(yr[c]));
-    xr[c] = xn;
-    const double v = bf16_to_f32(xn);
-    ss += v * v;
+  for (int c = threadIdx.x; c < h8; c += kCThreads) {
+    const u32x4 v = xr[c];
+    const f32x4 y0 = yr[2 * c], y1 = yr[2 * c + 1];
+    u32x4 n;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      const float ylo = w < 2 ? y0[2 * w] : y1[2 * w - 4];
+      const float yhi = w < 2 ? y0[2 * w + 1] : y1[2 * w - 3];
+      const uint32_t lo =
+          f64_to_bf16(static_cast<double>(bf16_to_f32(v[w] & 0xffffu)) + static_cast<double>(ylo));
+      const uint32_t hi =
+          f64_to_bf16(static_cast<double>(bf16_to_f32(v[w] >> 16)) + static_cast<double>(yhi));
+      n[w] = lo | (hi << 16);
+    }
+    xr[c] = n;
+    ss += sum_sq8(n);
   }
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) ss += __shfl_xor(ss, o);
-  if ((threadIdx.x & 63) == 0) part[threadIdx.x >> 6] = ss;
-  __syncthreads();
-  double tot = 0.0;
-#pragma unroll
-  for (int w = 0; w < kCThreads / 64; ++w) tot += part[w];
-  const double d = sqrt(tot / static_cast<double>(H) + 1e-6);
-  uint16_t* o = out + static_cast<size_t>(t) * H;
-  for (int c = threadIdx.x; c < H; c += kCThreads)  // this thread wrote xr[c] above
-    o[c] = f64_to_bf16(static_cast<double>(bf16_to_f32(xr[c])) / d);
+  const double d = sqrt(block_sum_f64(ss, part) / static_cast<double>(H) + 1e-6);
+  u32x4* o = reinterpret_cast<u32x4*>(out + static_cast<size_t>(blockIdx.x) * H);
+  for (int c = threadIdx.x; c < h8; c += kCThreads) o[c] = scale8(xr[c], d);  // written above by this thread
 }
 
 }  // namespace

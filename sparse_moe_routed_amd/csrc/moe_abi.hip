@@ -585,6 +585,8 @@ int32_t moe_quantize_activation(int32_t fmt, int32_t rows, int32_t cols, const v
 int32_t moe_prenorm(int32_t T, int32_t H, const void* x, void* out, void* stream) {
   if (T < 0 || T > kMaxTokens || H <= 0 || H % 64) return MOE_EINVAL;
   if (!x || !out) return MOE_EINVAL;
+  if (reinterpret_cast<uintptr_t>(x) % 16 || reinterpret_cast<uintptr_t>(out) % 16)
+    return MOE_EINVAL;  // rows move in 16-byte chunks
   if (T == 0) return MOE_OK;
   return hip_status(moe::launch_prenorm(static_cast<const uint16_t*>(x), T, H,
                                         static_cast<uint16_t*>(out),
@@ -603,6 +605,9 @@ int32_t moe_residual_prenorm(int32_t T, int32_t H, void* x, const float* y, void
                              void* stream) {
   if (T < 0 || T > kMaxTokens || H <= 0 || H % 64) return MOE_EINVAL;
   if (!x || !y || !out || out == x) return MOE_EINVAL;
+  if (reinterpret_cast<uintptr_t>(x) % 16 || reinterpret_cast<uintptr_t>(y) % 16 ||
+      reinterpret_cast<uintptr_t>(out) % 16)
+    return MOE_EINVAL;  // rows move in 16-byte chunks
   if (T == 0) return MOE_OK;
   return hip_status(moe::launch_residual_prenorm(static_cast<uint16_t*>(x), y, T, H,
                                                  static_cast<uint16_t*>(out),

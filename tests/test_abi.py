@@ -212,6 +212,13 @@ def test_quantize_validation(lib):
     assert rp(4, 64, FAKE, FAKE, FAKE, None) == moe.EINVAL  # out aliases x
     assert rp(4, 60, FAKE, FAKE, ctypes.c_void_p(FAKE.value + 4096), None) == moe.EINVAL
     assert rp(0, 64, FAKE, FAKE, ctypes.c_void_p(FAKE.value + 4096), None) == moe.OK
+    # rows move in 16-byte chunks: misaligned pointers are rejected
+    odd = ctypes.c_void_p(FAKE.value + 8)
+    assert lib.moe_prenorm(4, 64, odd, FAKE, None) == moe.EINVAL
+    assert lib.moe_prenorm(4, 64, FAKE, odd, None) == moe.EINVAL
+    assert rp(4, 64, odd, FAKE, ctypes.c_void_p(FAKE.value + 4096), None) == moe.EINVAL
+    assert rp(4, 64, FAKE, odd, ctypes.c_void_p(FAKE.value + 4096), None) == moe.EINVAL
+    assert rp(4, 64, FAKE, FAKE, ctypes.c_void_p(FAKE.value + 4104), None) == moe.EINVAL
 
 
 def test_binding_fails_loudly_without_library(monkeypatch):
