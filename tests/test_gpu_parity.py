@@ -20,6 +20,10 @@ TOL = {"bf16": 2e-2, "fp8": 5e-2, "nvfp4": 1e-1}
 FULL = synth.Dims()
 SMALL = synth.Dims(hidden=256, ffn=192, n_experts=32, top_k=4)
 WIDE = synth.Dims(hidden=128, ffn=128, n_experts=256, top_k=8)  # largest E and k supported
+# odd K-step counts: 3 steps of 64 along H (the FP8 up projection's last pair
+# of steps holds one step), 2.5 steps of 128 along F (the FP8 down panels'
+# 64-code last step), short last panels of 64 rows on both projections
+ODD = synth.Dims(hidden=192, ffn=320, n_experts=16, top_k=2)
 
 
 def _ld(d: synth.Dims) -> moe.LayerDims:
@@ -65,6 +69,11 @@ def small():
 @pytest.fixture(scope="module")
 def wide():
     return Layer(WIDE, 0)
+
+
+@pytest.fixture(scope="module")
+def odd():
+    return Layer(ODD, 0)
 
 
 def _x(T, dims, outliers=False):
@@ -199,6 +208,13 @@ def test_forward_max_experts_and_k(wide, fmt, T):
     same = np.array([sorted(a) == sorted(b) for a, b in zip(ids_g, ids_o)])
     assert np.all(same | (gap < om.NEAR_TIE))
     _forward_case(wide, fmt, T)
+
+
+@pytest.mark.parametrize("fmt", ["bf16", "fp8", "nvfp4"])
+@pytest.mark.parametrize("T", [5, 40, 600])
+def test_forward_odd_step_counts(odd, fmt, T):
+    # 5: narrow up tiles; 40: 128-column decode tiles; 600: prefill tiles
+    _forward_case(odd, fmt, T)
 
 
 @pytest.mark.parametrize("fmt", ["bf16", "fp8", "nvfp4"])
@@ -501,10 +517,20 @@ def test_fp8_panel_view_matches_the_abi_formula():
 
 @pytest.mark.parametrize("fmt", ["fp8", "nvfp4"])
 def test_weight_codes_bit_exact(full, fmt):
+    _check_weight_codes(full, fmt, (0, 77, 127))
+
+
+@pytest.mark.parametrize("fmt", ["fp8", "nvfp4"])
+def test_weight_codes_odd_shape(odd, fmt):
+    # short last panels (64 rows) and the FP8 down projection's 64-code last step
+    _check_weight_codes(odd, fmt, range(ODD.n_experts))
+
+
+def _check_weight_codes(full, fmt, experts):
     bank = full.bank(fmt)
     torch.cuda.synchronize()
-    H, F = FULL.hidden, FULL.ffn
-    for e in (0, 77, 127):
+    H, F = full.dims.hidden, full.dims.ffn
+    for e in experts:
         for name, w, (N, K) in (("up", full.up[e], (F, H)), ("down", full.down[e], (H, F))):
             wf = w.float().numpy()
             q_gpu = getattr(bank, name)[e].cpu().numpy()
