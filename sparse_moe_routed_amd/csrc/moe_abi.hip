@@ -435,17 +435,9 @@ int32_t forward_impl(const moe_dims* dims, int32_t T, const void* x, const int32
   // 2. token quantisation (fp8 / nvfp4)
   marks.mark(1);
   const void* a_up = x;
-  if (fmt == kFP8) {
-    err = moe::launch_amax_bf16(static_cast<const uint16_t*>(x), nullptr, T, H, amax_x, st);
-    if (err == hipSuccess)
-      err = moe::launch_quant_fp8(static_cast<const uint16_t*>(x), nullptr, T, H, amax_x, 0,
-                                  at<uint16_t>(ws, L.x_q), nullptr, scales + 0, st);
-    a_up = at<uint16_t>(ws, L.x_q);
-  } else if (fmt == kNVFP4) {
-    err = moe::launch_amax_bf16(static_cast<const uint16_t*>(x), nullptr, T, H, amax_x, st);
-    if (err == hipSuccess)
-      err = moe::launch_quant_nvfp4(static_cast<const uint16_t*>(x), nullptr, T, H, amax_x, 0,
-                                    at<uint16_t>(ws, L.x_q), nullptr, nullptr, scales + 0, st);
+  if (fmt == kFP8 || fmt == kNVFP4) {
+    err = moe::launch_quant_tensor(fmt, static_cast<const uint16_t*>(x), T, H, amax_x, 0,
+                                   at<uint16_t>(ws, L.x_q), nullptr, nullptr, scales + 0, st);
     a_up = at<uint16_t>(ws, L.x_q);
   }
   if (err != hipSuccess) return MOE_EHIP;
@@ -570,15 +562,8 @@ int32_t moe_quantize_activation(int32_t fmt, int32_t rows, int32_t cols, const v
   uint32_t* amax = static_cast<uint32_t*>(ws);  // kAmaxSlots words
   hipError_t err = moe::launch_zero_u32(amax, moe::kAmaxSlots, st);
   if (err == hipSuccess)
-    err = moe::launch_amax_bf16(static_cast<const uint16_t*>(x), nullptr, rows, cols, amax, st);
-  if (err == hipSuccess) {
-    if (fmt == kFP8)
-      err = moe::launch_quant_fp8(static_cast<const uint16_t*>(x), nullptr, rows, cols, amax, 1,
-                                  nullptr, static_cast<uint8_t*>(codes), scale, st);
-    else
-      err = moe::launch_quant_nvfp4(static_cast<const uint16_t*>(x), nullptr, rows, cols, amax, 1,
-                                    nullptr, static_cast<uint8_t*>(codes), bs, scale, st);
-  }
+    err = moe::launch_quant_tensor(fmt, static_cast<const uint16_t*>(x), rows, cols, amax, 1,
+                                   nullptr, static_cast<uint8_t*>(codes), bs, scale, st);
   return hip_status(err);
 }
 

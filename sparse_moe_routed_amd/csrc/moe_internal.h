@@ -119,6 +119,15 @@ hipError_t launch_zero_u32(uint32_t* p, int n, hipStream_t stream);
 hipError_t launch_combine(const float* rows, const int32_t* inv, int T, int k, int H, void* y,
                           int y_f32, hipStream_t stream);
 
+// Per-tensor quantisation of a whole bf16 tensor [rows, cols] (the tokens,
+// or moe_quantize_activation): amax into the zeroed slots `amax`, then codes
+// (FP8: mode 0 bf16 dec(code) into deq, mode 1 codes; NVFP4: mode 0 fp16
+// values into deq, mode 1 codes and block scales).  Small tensors run in one
+// workgroup that takes the amax itself and leaves the slots untouched.
+hipError_t launch_quant_tensor(int fmt, const uint16_t* x, int rows, int cols, uint32_t* amax,
+                               int mode, uint16_t* deq, uint8_t* codes, uint8_t* bs, float* scale,
+                               hipStream_t stream);
+
 // fp8_panels: write FP8 codes in the panel layout (down projection) rather
 // than row-major (up projection)
 hipError_t launch_quant_weights(int fmt, const uint16_t* w, int E, int N, int K, uint8_t* q,
