@@ -25,8 +25,11 @@ Parity status:
                    identity per expert (gate/index placement), textbook
                    single-expert FFN by per-token loops, dense masked sum over
                    all experts, linearity in the gates, expert relabelling
-  quantised paths  pinned through the codec pins plus exact all-ones and
-                   representable-value round trips
+  quantised paths  pinned through the codec pins, and by a per-token, per-slot
+                   loop over hand-dequantised operands for both halves: x
+                   quantised as one tensor, each expert projection on its own,
+                   the stacked intermediate [T*k, F] as one tensor (a loop that
+                   quantised it per expert, or not at all, fails the pin)
   prenorm/stack    prenorm pinned by closed form on constant rows; the stack
                    is composition only (the pre-norm is a reading: the literal residual
                    stack without normalisation diverges within a few layers)

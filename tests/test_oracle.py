@@ -239,11 +239,64 @@ def test_quantised_forward_matches_hand_dequantised():
                     Ue = codecs.nvfp4_dequantize(*codecs.nvfp4_quantize(U[e]))
                 a2[t * k + j] = codecs.bf16_rne(np.maximum(Ue @ xq[t], 0) ** 2)
         assert np.array_equal(a, a2)
+        # the down half by hand: the stacked intermediate [T*k, F] is quantised
+        # once as one tensor (one scale for all rows of all experts), each
+        # W_down per expert, then a per-token, per-slot loop in float64
+        if fmt == "fp8":
+            qa, sa = codecs.fp8_quantize(a2)
+            a2q = codecs.e4m3_decode(qa) * np.float64(sa)
+        else:
+            a2q = codecs.nvfp4_dequantize(*codecs.nvfp4_quantize(a2))
+        y2 = np.zeros_like(y)
+        for t in range(T):
+            for j in range(k):
+                e = ids[t, j]
+                if fmt == "fp8":
+                    qd, sd = codecs.fp8_quantize(D[e])
+                    De = codecs.e4m3_decode(qd) * np.float64(sd)
+                else:
+                    De = codecs.nvfp4_dequantize(*codecs.nvfp4_quantize(D[e]))
+                for o in range(De.shape[0]):
+                    y2[t, o] += g[t, j] * float(np.dot(De[o], a2q[t * k + j]))
+        assert np.allclose(y, y2, rtol=1e-12, atol=1e-12 * np.abs(y2).max())
         # different from the bf16 path (the quantisation is really applied)
         yb = om.forward(x, ids, g, om.ExpertBank(up, down, "bf16"))
         assert not np.allclose(y, yb, rtol=1e-3, atol=1e-3)
         rel = np.abs(y - yb).max() / np.sqrt(np.mean(yb ** 2))
         assert rel < (0.5 if fmt == "fp8" else 1.5)
+
+
+def test_quantised_intermediate_is_one_tensor():
+    # the intermediate scale is taken over all routed rows together: with one
+    # expert's rows made much larger than the others', quantising each
+    # expert's rows on their own would give the small rows finer codes
+    x, w, b, up, down, k = _small_layer(4, H=64, F=32)
+    T = x.shape[0]
+    ids = np.stack([np.arange(k) + (t % 2) * k for t in range(T)]).astype(np.int32)
+    g = np.full((T, k), 1.0 / k)
+    big = up.clone()
+    big[0] = big[0] * 8  # expert 0 (even tokens, slot 0): rows 64x larger after ReLU^2
+    for fmt in ("fp8", "nvfp4"):
+        bank = om.ExpertBank(big, down, fmt)
+        y, a = om.forward(x, ids, g, bank, return_a=True)
+        aq_tensor = om.quantise_activation(a, fmt)
+        per_expert = np.zeros_like(a)
+        for e in np.unique(ids):
+            rows = np.nonzero(ids.reshape(-1) == e)[0]
+            per_expert[rows] = om.quantise_activation(a[rows], fmt)
+        assert not np.array_equal(aq_tensor, per_expert)
+
+        def down_half(aq):
+            out = np.zeros_like(y)
+            for t in range(T):
+                for j in range(k):
+                    De = bank.down(int(ids[t, j]))
+                    out[t] += g[t, j] * (De @ aq[t * k + j])
+            return out
+
+        assert np.allclose(y, down_half(aq_tensor), rtol=1e-12, atol=1e-12 * np.abs(y).max())
+        assert not np.allclose(y, down_half(per_expert), rtol=1e-6, atol=0)
+        assert not np.allclose(y, down_half(a), rtol=1e-6, atol=0)
 
 
 def test_empty_batch():
