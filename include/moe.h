@@ -23,6 +23,11 @@
  *     moe_cache_init and moe_forward_cached, which wait for `stream`.
  *   - Row-major, contiguous layouts, except the packed NVFP4 expert bank
  *     (128-row panels, see moe_experts); bf16 is passed as raw 16-bit words.
+ *   - Alignment: token rows (x), outputs (y), router and expert weight codes
+ *     are read and written in 16-byte vectors, so those pointers must be
+ *     16-byte aligned; ids, gates, biases, scales and block scales 4-byte
+ *     aligned; FP8 activation codes 8-byte aligned.  A misaligned pointer
+ *     is MOE_EINVAL (hipMalloc and torch allocations are 256-byte aligned).
  *   - The caller owns every buffer.  The library allocates no device memory;
  *     scratch comes from the caller's workspace (moe_workspace_size).
  *   - Arguments are validated on the host before any launch.  On error the

@@ -38,6 +38,17 @@ bool dims_ok(const moe_dims* d) { return dims_check(d) == MOE_OK; }
 
 bool fmt_ok(int32_t fmt) { return fmt == kBF16 || fmt == kFP8 || fmt == kNVFP4; }
 
+bool aligned(const void* p, uintptr_t n) { return reinterpret_cast<uintptr_t>(p) % n == 0; }
+
+// The kernels move token rows, weight rows and output rows in 16-byte
+// vectors and routing entries, scales and block scales as 4-byte words.
+bool bank_aligned(const moe_experts* ex) {
+  if (!aligned(ex->up, 16) || !aligned(ex->down, 16)) return false;
+  if (ex->fmt != kBF16 && (!aligned(ex->up_s, 4) || !aligned(ex->down_s, 4))) return false;
+  if (ex->fmt == kNVFP4 && (!aligned(ex->up_bs, 4) || !aligned(ex->down_bs, 4))) return false;
+  return true;
+}
+
 struct Layout {
   size_t counts, offsets, scales, chunk_counts, chunk_base, tile_off0, tile_off1, sorted_src,
       inv, row_gate, act, out_rows, x_q, act_q, total;
@@ -254,6 +265,9 @@ int32_t moe_route(const moe_dims* dims, int32_t T, const void* x, const moe_rout
   if (T < 0 || T > kMaxTokens) return MOE_EINVAL;
   if (T == 0) return MOE_OK;  // nothing is read or written; pointers may be null
   if (!router || !router->w_packed || !x || !ids || !gates) return MOE_EINVAL;
+  if (!aligned(x, 16) || !aligned(router->w_packed, 16) || !aligned(router->bias, 4) ||
+      !aligned(ids, 4) || !aligned(gates, 4))
+    return MOE_EINVAL;
   const size_t need = static_cast<size_t>(moe::router_k_slices(T, dims->hidden)) * T *
                       dims->n_experts * 4;
   if (!ws || ws_bytes < need || reinterpret_cast<uintptr_t>(ws) % kAlign) return MOE_EWORKSPACE;
@@ -325,6 +339,9 @@ int32_t forward_impl(const moe_dims* dims, int32_t T, const void* x, const int32
   if (!x || !ids || !gates || !y || !ex->up || !ex->down) return MOE_EINVAL;
   if (ex->fmt != kBF16 && (!ex->up_s || !ex->down_s)) return MOE_EINVAL;
   if (ex->fmt == kNVFP4 && (!ex->up_bs || !ex->down_bs)) return MOE_EINVAL;
+  if (!aligned(x, 16) || !aligned(y, 16) || !aligned(ids, 4) || !aligned(gates, 4) ||
+      !bank_aligned(ex))
+    return MOE_EINVAL;
   const Layout L = make_layout(dims, ex->fmt, T);
   if (!ws || ws_bytes < L.total) return MOE_EWORKSPACE;
   if (reinterpret_cast<uintptr_t>(ws) % kAlign) return MOE_EWORKSPACE;
@@ -539,6 +556,10 @@ int32_t moe_quantize_experts(const moe_dims* dims, int32_t fmt, const void* up_b
   if (fmt != kFP8 && fmt != kNVFP4) return MOE_EINVAL;
   if (!up_bf16 || !down_bf16 || !up_q || !down_q || !up_s || !down_s) return MOE_EINVAL;
   if (fmt == kNVFP4 && (!up_bs || !down_bs)) return MOE_EINVAL;
+  if (!aligned(up_bf16, 16) || !aligned(down_bf16, 16) || !aligned(up_q, 16) ||
+      !aligned(down_q, 16) || !aligned(up_bs, 4) || !aligned(down_bs, 4) || !aligned(up_s, 4) ||
+      !aligned(down_s, 4))
+    return MOE_EINVAL;
   const hipStream_t st = static_cast<hipStream_t>(stream);
   const int H = dims->hidden, F = dims->ffn, E = dims->n_experts;
   hipError_t err = moe::launch_quant_weights(fmt, static_cast<const uint16_t*>(up_bf16), E, F, H,
@@ -556,7 +577,8 @@ int32_t moe_quantize_activation(int32_t fmt, int32_t rows, int32_t cols, const v
   if (rows < 0 || cols <= 0 || cols % 64) return MOE_EINVAL;
   if (static_cast<long long>(rows) * cols > (1ll << 31)) return MOE_EUNSUPPORTED;
   if (!x || !codes || !scale || (fmt == kNVFP4 && !bs)) return MOE_EINVAL;
-  if (!ws || ws_bytes < kAlign) return MOE_EWORKSPACE;
+  if (!aligned(x, 16) || !aligned(codes, 8) || !aligned(scale, 4)) return MOE_EINVAL;
+  if (!ws || ws_bytes < kAlign || !aligned(ws, 4)) return MOE_EWORKSPACE;
   if (rows == 0) return MOE_OK;
   const hipStream_t st = static_cast<hipStream_t>(stream);
   uint32_t* amax = static_cast<uint32_t*>(ws);  // kAmaxSlots words

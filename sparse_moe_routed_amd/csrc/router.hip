@@ -226,9 +226,11 @@ __device__ __forceinline__ uint32_t wave_umax(uint32_t v) {
 }
 
 // order-preserving unsigned key of a float (larger float -> larger key; -inf
-// maps above 0, which marks an empty slot)
+// maps above 0, which marks an empty slot).  -0 and +0 compare equal as
+// floats, so -0 is first made +0 (x + 0 is +0 for x = -0 under round to
+// nearest) and both get one key: a tie between them goes to the lower index.
 __device__ __forceinline__ uint32_t float_key(float f) {
-  const uint32_t u = __float_as_uint(f);
+  const uint32_t u = __float_as_uint(f + 0.0f);
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 

@@ -108,6 +108,12 @@ def test_route_validation(lib):
     assert call(ws=None) == moe.EWORKSPACE
     assert call(wsb=64) == moe.EWORKSPACE
     assert call(ws=ctypes.c_void_p(FAKE.value + 4)) == moe.EWORKSPACE
+    # rows move in 16-byte vectors, routing entries in 4-byte words
+    assert call(x=ctypes.c_void_p(FAKE.value + 8)) == moe.EINVAL
+    assert call(router=moe.Router(FAKE.value + 2, None)) == moe.EINVAL
+    assert call(router=moe.Router(FAKE.value, FAKE.value + 2)) == moe.EINVAL
+    assert call(ids=ctypes.c_void_p(FAKE.value + 2)) == moe.EINVAL
+    assert call(gates=ctypes.c_void_p(FAKE.value + 1)) == moe.EINVAL
     # T == 0 is a no-op that touches nothing
     assert call(T=0, x=None, ids=None, gates=None, ws=None, wsb=0) == moe.OK
     assert lib.moe_router_pack(ctypes.byref(d), None, FAKE, st) == moe.EINVAL
@@ -143,6 +149,20 @@ def test_forward_validation(lib):
     assert call(ws=None) == moe.EWORKSPACE
     assert call(wsb=need - 1) == moe.EWORKSPACE
     assert call(ws=ctypes.c_void_p(FAKE.value + 16)) == moe.EWORKSPACE
+    # alignment: token and output rows 16 bytes, ids / gates 4 bytes, weight
+    # codes 16 bytes, scales and block scales 4 bytes
+    off = lambda n: ctypes.c_void_p(FAKE.value + n)
+    assert call(x=off(8)) == moe.EINVAL
+    assert call(x=off(2)) == moe.EINVAL
+    assert call(y=off(4)) == moe.EINVAL
+    assert call(ids=off(2)) == moe.EINVAL
+    assert call(gates=off(2)) == moe.EINVAL
+    assert call(e=moe.Experts(0, FAKE.value + 8, FAKE.value, None, None, None, None)) == moe.EINVAL
+    assert call(e=moe.Experts(0, FAKE.value, FAKE.value + 2, None, None, None, None)) == moe.EINVAL
+    assert call(e=moe.Experts(1, FAKE.value, FAKE.value, None, None, FAKE.value + 2,
+                              FAKE.value)) == moe.EINVAL
+    assert call(e=moe.Experts(2, FAKE.value, FAKE.value, FAKE.value + 1, FAKE.value, FAKE.value,
+                              FAKE.value)) == moe.EINVAL
     # T == 0: nothing to do, no workspace needed
     assert call(T=0, ws=None, wsb=0) == moe.OK
     # the timed variant needs at least one event per stage boundary
@@ -196,7 +216,11 @@ def test_quantize_validation(lib):
     assert q(ctypes.byref(d), 0, FAKE, FAKE, FAKE, FAKE, None, None, FAKE, FAKE, None) == moe.EINVAL
     assert q(ctypes.byref(d), 2, FAKE, FAKE, FAKE, FAKE, None, None, FAKE, FAKE, None) == moe.EINVAL
     assert q(ctypes.byref(d), 1, None, FAKE, FAKE, FAKE, None, None, FAKE, FAKE, None) == moe.EINVAL
+    assert q(ctypes.byref(d), 1, ctypes.c_void_p(FAKE.value + 2), FAKE, FAKE, FAKE, None, None,
+             FAKE, FAKE, None) == moe.EINVAL
     a = lib.moe_quantize_activation
+    assert a(1, 4, 64, ctypes.c_void_p(FAKE.value + 2), FAKE, None, FAKE, FAKE, 256, None) == moe.EINVAL
+    assert a(1, 4, 64, FAKE, ctypes.c_void_p(FAKE.value + 4), None, FAKE, FAKE, 256, None) == moe.EINVAL
     assert a(0, 4, 64, FAKE, FAKE, None, FAKE, FAKE, 256, None) == moe.EINVAL
     assert a(1, 4, 60, FAKE, FAKE, None, FAKE, FAKE, 256, None) == moe.EINVAL
     assert a(2, 4, 64, FAKE, FAKE, None, FAKE, FAKE, 256, None) == moe.EINVAL
