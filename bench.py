@@ -24,7 +24,12 @@ expert bank in pinned host memory and N device slots (uploads included).
 Prints one JSON line.  `roofline` describes the dominant kernel (algorithmic
 bytes or flops per launch / the mean of its kernel's own start-to-end
 durations in the second pass); `cpu_baseline` is the CPU
-oracle timed on this host on a bounded sample of the same workload.
+oracle timed on this host on a bounded sample of the same workload; `parity`
+compares the timed run's output on those sampled tokens with the oracle's
+(max |delta| / rms, near ties counted, id sets compared).  A single-layer
+decode workload also carries a `prefill` record: the same measurement on the
+4096-token prefill batch of the same format (the MFMA half of the metric),
+unless --no-prefill.
 """
 from __future__ import annotations
 
@@ -43,6 +48,8 @@ METRIC = "MoE-layer tokens/s; HBM GB/s at T=64, MFMA TFLOP/s at T=4096 (1 GPU)"
 HBM_PEAK_GBS = 8000.0
 # nvfp4 runs on the fp16 MFMA after an exact expansion of its codes: same peak as bf16
 MFMA_PEAK_TFLOPS = {"bf16": 2500.0, "fp8": 5000.0, "nvfp4": 2500.0}
+# the card's dense 4-bit MFMA peak, reported beside the fp16 one for nvfp4
+FP4_PEAK_TFLOPS = 10100.0
 
 
 def parse():
@@ -52,6 +59,8 @@ def parse():
     p.add_argument("--warmup", type=int, default=30)
     p.add_argument("--workload", default="decode_t64_bf16")
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--no-prefill", action="store_true",
+                   help="skip the 4096-token prefill record of a decode workload")
     p.add_argument("--graph", action="store_true",
                    help="also capture one step into a HIP graph and time K replays "
                         "(reported beside the eager headline)")
@@ -166,48 +175,13 @@ def cached_bench(args, wl):
     print(json.dumps(out), flush=True)
 
 
-def main():
-    args = parse()
-    world = int(os.environ.get("WORLD_SIZE", "1"))
-    if args.gpus > 1 or world > 1:
-        print(f"bench.py: measures one GPU only; --gpus {max(args.gpus, world)} "
-              "is not supported (the layer would shard by expert parallelism; only the "
-              "single-GPU kernels are built)",
-              file=sys.stderr)
-        sys.exit(2)
-
-    import numpy as np
+def build_layers(fmt, n_layers, dev, ld, verbose=True):
+    """Router and expert bank of each layer on the device (seeded synthetic)."""
     import torch
 
     import sparse_moe_routed_amd as moe
     from sparse_moe_routed_amd import synth
 
-    if args.copy_calibration:
-        n = 1 << 30
-        src = torch.ones(n, dtype=torch.uint8, device="cuda")
-        dst = torch.empty_like(src)
-        for _ in range(args.steps):
-            dst.copy_(src)
-        torch.cuda.synchronize()
-        print(json.dumps({"copy_calibration_bytes_each_way": n, "launches": args.steps}), flush=True)
-        return
-
-    if args.workload not in synth.WORKLOADS:
-        sys.exit(f"unknown workload {args.workload}; choose from {sorted(synth.WORKLOADS)}")
-    wl = synth.WORKLOADS[args.workload]
-    T, fmt, n_layers = wl["T"], wl["fmt"], wl["layers"]
-    if args.cache_slots:
-        if n_layers != 1:
-            sys.exit("--cache-slots applies to single-layer workloads")
-        return cached_bench(args, wl)
-    dims = synth.Dims()
-    ld = moe.LayerDims()
-    H, F, E, k = dims.hidden, dims.ffn, dims.n_experts, dims.top_k
-    assert torch.cuda.is_available(), "bench.py needs a GPU"
-    dev = torch.device("cuda:0")
-    hip = Hip()
-
-    # ---------------------------------------------------------------- inputs
     t_setup = time.time()
     layers = []
     for l in range(n_layers):
@@ -219,7 +193,28 @@ def main():
         if fmt != "bf16":
             del up_d, down_d
         layers.append(dict(router=moe.pack_router(w_r.to(dev), b.to(dev), ld), bank=bank))
-        print(f"# layer {l} ready ({time.time() - t_setup:.1f}s)", file=sys.stderr, flush=True)
+        if verbose:
+            print(f"# {fmt} layer {l} ready ({time.time() - t_setup:.1f}s)", file=sys.stderr, flush=True)
+    torch.cuda.synchronize()
+    return layers
+
+
+def measure(args, name, layers, hip):
+    """Time one workload (see the module docstring).  Returns (record, state):
+    the record of the bench line without its headline keys, and the device
+    tensors of the last step for the parity check."""
+    import numpy as np
+    import torch
+
+    import sparse_moe_routed_amd as moe
+    from sparse_moe_routed_amd import synth
+
+    wl = synth.WORKLOADS[name]
+    T, fmt, n_layers = wl["T"], wl["fmt"], wl["layers"]
+    dims = synth.Dims()
+    ld = moe.LayerDims()
+    H, F, E, k = dims.hidden, dims.ffn, dims.n_experts, dims.top_k
+    dev = torch.device("cuda:0")
     x0 = synth.make_tokens(T, outliers=wl["outliers"]).to(dev)
     ws = moe.workspace(ld, fmt, T, dev)
     rws = moe.route_workspace(ld, T, dev)
@@ -271,6 +266,9 @@ def main():
     wall = time.perf_counter() - t0
     ms_per_step = wall * 1e3 / args.steps
     tokens_per_s = T * args.steps / wall
+    # the last step's routing and output (single layer: the timed run's own
+    # result for x0; every step computes the same)
+    state = dict(ids=ids.clone(), gates=gates.clone(), y=y.clone(), x0=x0)
 
     # pass 2 (attribution): K more steps with HIP events at every stage
     # boundary, recorded on the stream the kernels run on (events add a few
@@ -278,7 +276,6 @@ def main():
     # two GEMM launches themselves: hipExtLaunchKernel stamps those events
     # with the kernel's own start and end, the interval a kernel trace reports
     # (stacked workloads: events around every layer, averaged over the layers)
-    timed_stages = True
     stage_ms = {}
     # Before each step a 512 MB buffer is read (outside the events), more than
     # the 256 MB Infinity Cache, so no step finds the previous step's weights
@@ -294,8 +291,8 @@ def main():
     torch.cuda.synchronize()
     flat = [e for per_step in evs for e in per_step]
     stage_ms["route"] = float(np.mean([hip.elapsed(er[0], er[1]) for er, _ in flat]))
-    for si, name in enumerate(moe.STAGES):
-        stage_ms[name] = float(np.mean([hip.elapsed(es[si], es[si + 1]) for _, es in flat]))
+    for si, sname in enumerate(moe.STAGES):
+        stage_ms[sname] = float(np.mean([hip.elapsed(es[si], es[si + 1]) for _, es in flat]))
     j0 = moe.N_STAGES + 1
     gemm_kernel_ms = {
         "up": float(np.mean([hip.elapsed(es[j0], es[j0 + 1]) for _, es in flat])),
@@ -319,7 +316,7 @@ def main():
     for a, b in ev2:
         hip.destroy(a)
         hip.destroy(b)
-    q = lambda p: step_ev[min(len(step_ev) - 1, int(round(p * (len(step_ev) - 1))))]
+    q = lambda p_: step_ev[min(len(step_ev) - 1, int(round(p_ * (len(step_ev) - 1))))]
     step_pct = {"p10": round(q(0.1), 4), "p50": round(q(0.5), 4), "p90": round(q(0.9), 4)}
 
     # pass 4 (optional): the same step captured once into a HIP graph (the
@@ -356,51 +353,45 @@ def main():
     act_in_bytes = {"bf16": 2, "fp8": 1, "nvfp4": 2}[fmt]
     layer_bytes = touched * 2 * wbe + E * H * 4 + E * 4 + T * H * 2 + T * H * 4
     flops_up = 2.0 * R * F * H
-    roof = None
-    if timed_stages:
-        dom = "up" if gemm_kernel_ms["up"] >= gemm_kernel_ms["down"] else "down"
-        dur_s = gemm_kernel_ms[dom] * 1e-3
-        if T <= 256:
-            # weight-streaming launch: bytes of the touched experts' panels plus
-            # its activation input and output
-            if dom == "up":
-                alg = touched * wbe + T * H * act_in_bytes + R * F * 2
-            else:
-                alg = touched * wbe + R * F * act_in_bytes + R * H * 4
-            achieved = alg / dur_s / 1e9
-            roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
-                    "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                    "traffic": None, "kernel": f"grouped_gemm_{dom}", "alg_bytes": int(alg)}
+    dom = "up" if gemm_kernel_ms["up"] >= gemm_kernel_ms["down"] else "down"
+    dur_s = gemm_kernel_ms[dom] * 1e-3
+    if T <= 256:
+        # weight-streaming launch: bytes of the touched experts' panels plus
+        # its activation input and output
+        if dom == "up":
+            alg = touched * wbe + T * H * act_in_bytes + R * F * 2
         else:
-            achieved = flops_up / dur_s / 1e12
-            peak = MFMA_PEAK_TFLOPS[fmt]
-            roof = {"bound": "mfma", "achieved": round(achieved, 1), "peak": peak,
-                    "unit": "TFLOP/s", "frac": round(achieved / peak, 4), "traffic": None,
-                    "kernel": f"grouped_gemm_{dom}", "alg_flops": flops_up}
-        # HBM bytes per launch from the FETCH_SIZE / WRITE_SIZE counter passes,
-        # used only while the GEMM sources are the ones the counters were taken on
-        tf = os.path.join(ROOT, "profiles", f"traffic_{args.workload}.json")
-        if os.path.exists(tf):
-            rec = json.load(open(tf))
-            if rec.get("source_sha256") == gemm_source_sha256():
-                roof["traffic"] = rec.get("bytes_per_launch", {}).get(roof["kernel"])
+            alg = touched * wbe + R * F * act_in_bytes + R * H * 4
+        achieved = alg / dur_s / 1e9
+        roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
+                "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                "traffic": None, "kernel": f"grouped_gemm_{dom}", "alg_bytes": int(alg)}
+    else:
+        achieved = flops_up / dur_s / 1e12
+        peak = MFMA_PEAK_TFLOPS[fmt]
+        roof = {"bound": "mfma", "achieved": round(achieved, 1), "peak": peak,
+                "unit": "TFLOP/s", "frac": round(achieved / peak, 4), "traffic": None,
+                "kernel": f"grouped_gemm_{dom}", "alg_flops": flops_up,
+                "mfma": {"bf16": "bf16", "fp8": "fp8 (down), bf16 on expanded codes (up)",
+                         "nvfp4": "f16 on exactly expanded codes"}[fmt]}
+        if fmt == "nvfp4":
+            roof["peak_fp4"] = FP4_PEAK_TFLOPS
+            roof["frac_fp4"] = round(achieved / FP4_PEAK_TFLOPS, 4)
+    # HBM bytes per launch from the FETCH_SIZE / WRITE_SIZE counter passes,
+    # used only while the GEMM sources are the ones the counters were taken on
+    tf = os.path.join(ROOT, "profiles", f"traffic_{name}.json")
+    if os.path.exists(tf):
+        rec = json.load(open(tf))
+        if rec.get("source_sha256") == gemm_source_sha256():
+            roof["traffic"] = rec.get("bytes_per_launch", {}).get(roof["kernel"])
 
     layer_ms = ms_per_step / n_layers
     out = {
-        "metric": METRIC,
         "value": round(tokens_per_s, 1),
-        "unit": "tokens/s",
-        "n_gpus": 1,
-        "steps": args.steps,
-        "warmup": args.warmup,
         "ms_per_step": round(ms_per_step, 4),
-        "higher_is_better": True,
-        "scaling": "weak",
-        "vs_baseline": None,
         "dtype": fmt,
-        "data": "synthetic (seeded; shapes and distributions of the Nemotron 3.5 Transcribe routed MoE layer)",
-        "config": {"workload": args.workload, "T": T, "hidden": H, "ffn": F, "experts": E,
-                   "top_k": k, "format": fmt, "layers": n_layers},
+        "config": {"workload": name, "T": T, "hidden": H, "ffn": F, "experts": E,
+                   "top_k": k, "format": fmt, "layers": n_layers, "outlier_rows": wl["outliers"]},
         "layer_hbm_gbs": round(layer_bytes / (layer_ms * 1e-3) / 1e9, 1),
         "layer_tflops": round(2 * flops_up / (layer_ms * 1e-3) / 1e12, 2),
         "experts_touched": touched,
@@ -411,10 +402,84 @@ def main():
     }
     if graph_rec:
         out["graph"] = graph_rec
+    return out, state
 
-    # ---------------------------------------------------------------- CPU oracle
+
+def main():
+    args = parse()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus > 1 or world > 1:
+        print(f"bench.py: measures one GPU only; --gpus {max(args.gpus, world)} "
+              "is not supported (the layer would shard by expert parallelism; only the "
+              "single-GPU kernels are built)",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import sparse_moe_routed_amd as moe
+    from sparse_moe_routed_amd import synth
+
+    if args.copy_calibration:
+        n = 1 << 30
+        src = torch.ones(n, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(args.steps):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calibration_bytes_each_way": n, "launches": args.steps}), flush=True)
+        return
+
+    if args.workload not in synth.WORKLOADS:
+        sys.exit(f"unknown workload {args.workload}; choose from {sorted(synth.WORKLOADS)}")
+    wl = synth.WORKLOADS[args.workload]
+    fmt, n_layers = wl["fmt"], wl["layers"]
+    if args.cache_slots:
+        if n_layers != 1:
+            sys.exit("--cache-slots applies to single-layer workloads")
+        return cached_bench(args, wl)
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    dev = torch.device("cuda:0")
+    hip = Hip()
+    ld = moe.LayerDims()
+
+    layers = build_layers(fmt, n_layers, dev, ld)
+    rec, state = measure(args, args.workload, layers, hip)
+    out = {
+        "metric": METRIC,
+        "value": rec.pop("value"),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": rec.pop("ms_per_step"),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": rec.pop("dtype"),
+        "data": "synthetic (seeded; shapes and distributions of the Nemotron 3.5 Transcribe routed MoE layer)",
+        "config": rec.pop("config"),
+    }
+    out.update(rec)
     if not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline(args, wl, dims)
+        out["cpu_baseline"], out["parity"] = cpu_baseline(args.workload, state)
+        if n_layers > 1:
+            # the timed step ends with the last layer's output; per-layer
+            # parity of the stack is a GPU test (teacher-forced)
+            out["parity"] = None
+
+    # the MFMA half of the metric: the 4096-token prefill batch of the same
+    # format, with the same layer weights
+    pre = f"prefill_t4096_{fmt}"
+    if (not args.no_prefill and n_layers == 1 and wl["T"] < 4096 and pre in synth.WORKLOADS
+            and synth.WORKLOADS[pre]["layers"] == 1):
+        del state
+        torch.cuda.empty_cache()
+        prec, pstate = measure(args, pre, layers, hip)
+        if not args.no_cpu_baseline:
+            prec["cpu_baseline"], prec["parity"] = cpu_baseline(pre, pstate)
+        prec.pop("dtype")
+        out["prefill"] = prec
     print(json.dumps(out), flush=True)
 
 
@@ -426,37 +491,80 @@ def gemm_source_sha256():
     return h.hexdigest()
 
 
-def cpu_baseline(args, wl, dims):
-    """The oracle as it stands, on a bounded token sample of the same workload."""
+def cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def cpu_baseline(name, state):
+    """The oracle as it stands, on a bounded token sample of the same workload,
+    and the parity of the timed run's output on that sample: the oracle routes
+    the sampled tokens itself (float64); tokens whose 6th/7th logit gap is
+    under 1e-5 are near ties (counted; left out if their id sets differ), the
+    other id sets must equal the GPU's, and the outputs are compared on the
+    tokens with equal id sets (the oracle's own routing and gates)."""
     import numpy as np
     from threadpoolctl import threadpool_info
 
     from oracle import moe as om
     from sparse_moe_routed_amd import synth
 
-    T = wl["T"]
+    wl = synth.WORKLOADS[name]
+    T, fmt = wl["T"], wl["fmt"]
     x = synth.make_tokens(T, outliers=wl["outliers"]).float().numpy()
     w_r, b = synth.make_router(0)
-    up, down = synth.make_experts(0)
-    bank = om.ExpertBank(up, down, wl["fmt"])
-    # bf16: the whole batch; fp8/nvfp4: the oracle re-quantises every touched
-    # expert on each call, so a few tokens already cost tens of seconds
-    n = T if wl["fmt"] == "bf16" else min(T, 4)
-    xs = x[:n]
+    # bf16: the oracle needs no dequantisation, so a larger sample (the whole
+    # decode batch; 192 tokens of a prefill batch, every 8th outlier row among
+    # them); fp8/nvfp4: the oracle re-quantises every touched expert on each
+    # call, so a few tokens already cost tens of seconds
+    if fmt == "bf16":
+        n = min(T, 192)
+    else:
+        n = min(T, 4)
+    rng = np.random.default_rng(77)
+    sample = np.arange(T) if n == T else np.sort(rng.choice(T, n, replace=False))
+    xs = x[sample]
+    # only the experts the sample can touch are generated (each from its own stream)
+    ids_o, _, _, _ = om.route(xs, w_r.numpy(), b.numpy(), synth.TOP_K)
+    touched = np.unique(ids_o)
+    up, down = synth.make_experts(0, experts=touched)
+    pos = {int(e): i for i, e in enumerate(touched)}
+    bank = om.ExpertBank({e: up[i] for e, i in pos.items()}, {e: down[i] for e, i in pos.items()},
+                         fmt)
     # repeat the sample until about ten seconds of CPU work have been timed
     spent, done_tokens, passes = 0.0, 0, 0
+    y_o = ids_o = g_o = gap = None
     while spent < 10.0 and passes < 100:
         t0 = time.perf_counter()
-        ids, g, _, _ = om.route(xs, w_r.numpy(), b.numpy(), dims.top_k)
-        om.forward(xs, ids, g, bank)
+        ids_o, g_o, gap, _ = om.route(xs, w_r.numpy(), b.numpy(), synth.TOP_K)
+        y_o = om.forward(xs, ids_o, g_o, bank)
         spent += time.perf_counter() - t0
         done_tokens += n
         passes += 1
     threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
-    return {"value": round(done_tokens / spent, 3), "unit": "tokens/s", "cores": int(threads),
-            "kind": "oracle",
+    base = {"value": round(done_tokens / spent, 3), "unit": "tokens/s", "cores": int(threads),
+            "kind": "oracle", "cpu_model": cpu_model(),
             "sample": f"{passes} pass(es) over {n} tokens of the {T}-token batch (float64 NumPy, "
-                      f"one layer, {wl['fmt']} weights dequantised by the oracle), {spent:.1f}s"}
+                      f"one layer, {fmt} weights dequantised by the oracle), {spent:.1f}s"}
+    # parity of the timed run's output on the sample
+    ids_g = state["ids"].cpu().numpy()[sample]
+    y_g = state["y"].double().cpu().numpy()[sample]
+    near = gap < om.NEAR_TIE
+    same = np.array([sorted(p_) == sorted(q_) for p_, q_ in zip(ids_g, ids_o)])
+    rms = float(np.sqrt(np.mean(y_o[same] ** 2))) if same.any() else float("nan")
+    err = float(np.abs(y_g[same] - y_o[same]).max() / rms) if same.any() else float("nan")
+    tol = {"bf16": 2e-2, "fp8": 5e-2, "nvfp4": 1e-1}[fmt]
+    parity = {"tokens": int(n), "max_abs_delta_over_rms": err, "tolerance": tol,
+              "within_tolerance": bool(err <= tol), "near_ties": int(near.sum()),
+              "id_set_mismatches": int((~same & ~near).sum()),
+              "near_tie_mismatches": int((~same & near).sum()),
+              "compared": "fp32 y of the timed run vs the float64 oracle (own routing and gates)"}
+    return base, parity
 
 
 if __name__ == "__main__":
