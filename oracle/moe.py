@@ -30,6 +30,9 @@ Parity status:
                    quantised as one tensor, each expert projection on its own,
                    the stacked intermediate [T*k, F] as one tensor (a loop that
                    quantised it per expert, or not at all, fails the pin)
+  shared_expert    pinned: per-token textbook loop (bf16) and hand-dequantised
+                   loop with its own intermediate tensor scale (fp8, nvfp4);
+                   identity weights bit-exact; block = routed + shared
   prenorm/stack    prenorm pinned by closed form on constant rows; the stack
                    is composition only (the pre-norm is a reading: the literal residual
                    stack without normalisation diverges within a few layers)
@@ -189,6 +192,29 @@ def layer(x, w_r, bias, bank: ExpertBank, k: int):
     """Route then run the experts: y float64 [T, H], plus the routing."""
     ids, gates, gap, _ = route(x, w_r, bias, k)
     return forward(x, ids, gates, bank), ids, gates, gap
+
+
+# --------------------------------------------------------------------------- shared expert
+def shared_expert(x, up, down, fmt: str = "bf16"):
+    """Shared expert beside the routed ones: one ungated ReLU^2 FFN applied
+    to every token with weight 1, y_s,t = W_down,s . a~_t with
+    a = bf16(relu(W_up,s . x~_t)^2).  In the quantised formats its activations
+    are quantised like a routed expert's: x~ per tensor over all of x, a~ per
+    tensor over its own intermediate [T, F_s] (a tensor of its own, apart
+    from the routed intermediate).  up bf16 [F_s, H], down bf16 [H, F_s].
+    The pages keep shared experts on the card beside the routed ones and give
+    no width for them (bloomery issue #967, section 4 "Placement on card,
+    host RAM and NVMe"); the width is the caller's."""
+    x = np.asarray(x, dtype=np.float64)
+    T = x.shape[0]
+    ids = np.zeros((T, 1), np.int32)
+    return forward(x, ids, np.ones((T, 1)), ExpertBank(up[None], down[None], fmt))
+
+
+def block(x, w_r, bias, bank: ExpertBank, shared_up, shared_down, k: int):
+    """The MoE block: routed layer plus the shared expert, y = y_routed + y_s."""
+    y, ids, gates, gap = layer(x, w_r, bias, bank, k)
+    return y + shared_expert(x, shared_up, shared_down, bank.fmt), ids, gates, gap
 
 
 # --------------------------------------------------------------------------- stacked path

@@ -299,6 +299,71 @@ def test_quantised_intermediate_is_one_tensor():
         assert not np.allclose(y, down_half(a), rtol=1e-6, atol=0)
 
 
+def test_shared_expert_textbook_and_quantised_loops():
+    # the shared expert is an FFN on every token with weight 1; in the
+    # quantised formats x is quantised as one tensor and the shared
+    # intermediate [T, F_s] as a tensor of its own
+    H, Fs, T = 48, 32, 7
+    rng = np.random.default_rng(21)
+    up = _bf16(rng.normal(0, 1 / math.sqrt(H), (Fs, H)))
+    down = _bf16(rng.normal(0, 1 / math.sqrt(Fs), (H, Fs)))
+    x = _x(T, H, 22)
+    U = up.float().numpy().astype(np.float64)
+    D = down.float().numpy().astype(np.float64)
+    for fmt in ("bf16", "fp8", "nvfp4"):
+        y = om.shared_expert(x, up, down, fmt)
+        if fmt == "bf16":
+            xq, Uq, Dq = x, U, D
+        elif fmt == "fp8":
+            qx, sx = codecs.fp8_quantize(x)
+            xq = codecs.e4m3_decode(qx) * np.float64(sx)
+            qu, su = codecs.fp8_quantize(U)
+            Uq = codecs.e4m3_decode(qu) * np.float64(su)
+            qd, sd = codecs.fp8_quantize(D)
+            Dq = codecs.e4m3_decode(qd) * np.float64(sd)
+        else:
+            xq = codecs.nvfp4_dequantize(*codecs.nvfp4_quantize(x))
+            Uq = codecs.nvfp4_dequantize(*codecs.nvfp4_quantize(U))
+            Dq = codecs.nvfp4_dequantize(*codecs.nvfp4_quantize(D))
+        a = np.zeros((T, Fs))
+        for t in range(T):
+            for f in range(Fs):
+                h = 0.0
+                for i in range(H):
+                    h += Uq[f, i] * xq[t, i]
+                a[t, f] = float(codecs.bf16_rne(np.array([max(h, 0.0) ** 2]))[0])
+        if fmt == "fp8":
+            qa, sa = codecs.fp8_quantize(a)
+            aq = codecs.e4m3_decode(qa) * np.float64(sa)
+        elif fmt == "nvfp4":
+            aq = codecs.nvfp4_dequantize(*codecs.nvfp4_quantize(a))
+        else:
+            aq = a
+        for t in range(T):
+            for o in range(H):
+                acc = 0.0
+                for f in range(Fs):
+                    acc += Dq[o, f] * aq[t, f]
+                assert abs(y[t, o] - acc) <= 1e-12 * (1 + abs(acc)), (fmt, t, o)
+
+
+def test_shared_expert_identity_and_block_sum():
+    # identity weights: y_s = bf16(relu(x)^2) on the first F_s dims, exactly
+    H, Fs, T = 48, 32, 9
+    up, down = _identity_bank(1, H, Fs)
+    x = _x(T, H, 23, scale=2.0)
+    y = om.shared_expert(x, up[0], down[0])
+    assert np.array_equal(y[:, :Fs], codecs.bf16_rne(np.maximum(x[:, :Fs], 0) ** 2))
+    assert not y[:, Fs:].any()
+    # the block is the routed layer plus the shared expert
+    x, w, b, upr, downr, k = _small_layer(5, H=48, F=32)
+    bank = om.ExpertBank(upr, downr)
+    yb, ids, g, _ = om.block(x, w, b, bank, up[0], down[0], k)
+    yr, ids2, g2, _ = om.layer(x, w, b, bank, k)
+    assert np.array_equal(ids, ids2)
+    assert np.allclose(yb - yr, om.shared_expert(x, up[0], down[0]), rtol=1e-12, atol=1e-12)
+
+
 def test_empty_batch():
     x, w, b, up, down, k = _small_layer()
     y = om.forward(x[:0], np.zeros((0, k), np.int32), np.zeros((0, k)), om.ExpertBank(up, down))
