@@ -53,7 +53,7 @@
 extern "C" {
 #endif
 
-#define MOE_ABI_VERSION 5
+#define MOE_ABI_VERSION 6
 
 typedef enum {
   MOE_OK = 0,
@@ -197,6 +197,30 @@ int32_t moe_forward_timed(const moe_dims* dims, int32_t T, const void* x,
                           void* ws, size_t ws_bytes, void* stream,
                           void* const* events, int32_t n_events);
 
+/* ---- shared expert
+ * The pages' decoder keeps shared experts on the card beside the routed ones
+ * (bloomery issue #967, section 4 "Placement on card, host RAM and NVMe");
+ * they give no width for them.  A shared expert is one ungated ReLU^2 FFN
+ * that every token takes with weight 1:
+ *   y_t (+)= W_down,s . a~_t,   a = bf16(relu(W_up,s . x~_t)^2)
+ * with x~ quantised as in moe_forward (per tensor over x) and a~ per tensor
+ * over the shared intermediate [T, F_s] on its own (FP8, NVFP4).
+ *   dims   [host] {H, F_s, 1, 1}: hidden width, shared-expert width, one
+ *          expert, one slot (MOE_EINVAL otherwise); H, F_s multiples of 64
+ *   x      [dev] bf16 [T, H]
+ *   expert [host] struct of [dev] pointers: a one-expert bank in the layouts
+ *          of moe_experts (E = 1; moe_quantize_experts packs it)
+ *   y      [dev] [T, H]: written (accumulate = 0; bf16 or fp32), or with
+ *          accumulate = 1 the fp32 result is added to the fp32 values y holds
+ *          (y_dtype must be MOE_Y_F32): after moe_forward into y this gives
+ *          the MoE block, routed + shared
+ *   ws     [dev] workspace of ws_bytes >= moe_shared_workspace_size(dims, fmt, T)
+ * Errors as moe_forward; T == 0 is a no-op. */
+size_t moe_shared_workspace_size(const moe_dims* dims, int32_t fmt, int32_t max_tokens);
+int32_t moe_shared_forward(const moe_dims* dims, int32_t T, const void* x,
+                           const moe_experts* expert, void* y, int32_t y_dtype,
+                           int32_t accumulate, void* ws, size_t ws_bytes, void* stream);
+
 /* ---- expert residency split
  * The routed expert banks stay in host memory in their stored format; the
  * experts a batch selects are uploaded into a bounded cache of device slots,
@@ -281,8 +305,9 @@ typedef struct {
 int32_t moe_workspace_layout(const moe_dims* dims, int32_t fmt, int32_t T,
                              moe_ws_layout* out /* [host] */);
 
-/* Pack a bf16 expert bank into FP8 or NVFP4 on the device, one fp32 scale per
- * expert projection (recipes: s = f32(amax/448), code = E4M3(f32(w*f32(448/amax)))
+/* Pack a bf16 expert bank into FP8 or NVFP4 on the device (any expert count
+ * 1 <= E <= 256, e.g. a shared expert's one-expert bank; top_k is not used),
+ * one fp32 scale per expert projection (recipes: s = f32(amax/448), code = E4M3(f32(w*f32(448/amax)))
  * for FP8; S = f32(amax/2688), block scale sb = E4M3(f32(amax_b/f32(6S))),
  * code = E2M1(f32(w*f32(1/f32(sb*S)))) for NVFP4; amax == 0 -> zero codes and
  * scale).  Layouts as in moe_experts.

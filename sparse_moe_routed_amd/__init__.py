@@ -88,6 +88,12 @@ _SIGS = {
                                            ctypes.c_void_p, ctypes.c_int32, ctypes.c_void_p,
                                            ctypes.c_size_t, ctypes.c_void_p,
                                            ctypes.POINTER(ctypes.c_void_p), ctypes.c_int32]),
+    "moe_shared_workspace_size": (ctypes.c_size_t, [ctypes.POINTER(Dims), ctypes.c_int32,
+                                                    ctypes.c_int32]),
+    "moe_shared_forward": (ctypes.c_int32, [ctypes.POINTER(Dims), ctypes.c_int32, ctypes.c_void_p,
+                                            ctypes.POINTER(Experts), ctypes.c_void_p, ctypes.c_int32,
+                                            ctypes.c_int32, ctypes.c_void_p, ctypes.c_size_t,
+                                            ctypes.c_void_p]),
     "moe_cache_state_size": (ctypes.c_size_t, [ctypes.POINTER(Dims), ctypes.c_int32]),
     "moe_cache_init": (ctypes.c_int32, [ctypes.POINTER(Dims), ctypes.POINTER(Cache), ctypes.c_void_p,
                                         ctypes.c_size_t, ctypes.c_void_p]),
@@ -113,7 +119,7 @@ _SIGS = {
 }
 
 _lib = None
-ABI_VERSION = 5  # MOE_ABI_VERSION of include/moe.h this binding describes
+ABI_VERSION = 6  # MOE_ABI_VERSION of include/moe.h this binding describes
 
 
 def lib():
@@ -284,6 +290,43 @@ def forward(x: torch.Tensor, ids: torch.Tensor, gates: torch.Tensor, experts: Ex
     _check("moe_forward", lib().moe_forward(ctypes.byref(d), T, _ptr(x), _ptr(ids), _ptr(gates),
                                             ctypes.byref(e), _ptr(y), yd, _ptr(ws),
                                             ws.numel(), _stream()))
+    return y
+
+
+def shared_dims(hidden: int = 2688, ffn: int = 3712) -> LayerDims:
+    """Dims of a shared expert: one expert that every token takes."""
+    return LayerDims(hidden, ffn, 1, 1)
+
+
+def shared_workspace(dims: LayerDims, fmt: str, max_tokens: int, device="cuda") -> torch.Tensor:
+    d = dims.c()
+    n = int(lib().moe_shared_workspace_size(ctypes.byref(d), WFMT[fmt], int(max_tokens)))
+    if n == 0:
+        raise ValueError(f"moe_shared_workspace_size: invalid dims {dims} or format {fmt}")
+    return torch.empty(n, dtype=torch.uint8, device=device)
+
+
+def shared_forward(x: torch.Tensor, expert: ExpertBank, dims: LayerDims,
+                   y: Optional[torch.Tensor] = None, y_dtype: torch.dtype = torch.float32,
+                   accumulate: bool = False, ws: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """moe_shared_forward: the shared expert on every token; with accumulate,
+    added to the fp32 y given (the routed output, for the MoE block)."""
+    T = x.shape[0]
+    _dev(x, torch.bfloat16, "x", (T, dims.hidden))
+    if y is None:
+        if accumulate:
+            raise ValueError("accumulate needs the y to add to")
+        y = torch.empty((T, dims.hidden), dtype=y_dtype, device=x.device)
+    _dev(y, y_dtype, "y", (T, dims.hidden))
+    if ws is None:
+        ws = shared_workspace(dims, expert.fmt, T, x.device)
+    _dev(ws, torch.uint8, "ws")
+    yd = {torch.float32: Y_F32, torch.bfloat16: Y_BF16}[y_dtype]
+    d = dims.c()
+    e = expert.c()
+    _check("moe_shared_forward", lib().moe_shared_forward(
+        ctypes.byref(d), T, _ptr(x), ctypes.byref(e), _ptr(y), yd, int(bool(accumulate)),
+        _ptr(ws), ws.numel(), _stream()))
     return y
 
 

@@ -19,10 +19,12 @@ constexpr int kCThreads = 256;
 // tid, stepping by G * kCThreads (G spreads a token over several workgroups
 // for small batches).  The K row loads of a group are issued together (a
 // dropped slot reads row 0 and is not added), then added in slot order.
+// y_mode: kYBF16 writes bf16, kYF32 fp32, kYF32Add adds the sum to the fp32
+// values y already holds (y_t + sum, one fp32 addition).
 template <int K>
 __global__ __launch_bounds__(kCThreads) void combine_kernel(const float* __restrict__ rows,
                                                             const int32_t* __restrict__ inv,
-                                                            int H, void* y, int y_f32) {
+                                                            int H, void* y, int y_mode) {
   const int t = blockIdx.x;
   int src[K];
 #pragma unroll
@@ -37,8 +39,10 @@ __global__ __launch_bounds__(kCThreads) void combine_kernel(const float* __restr
 #pragma unroll
     for (int j = 0; j < K; ++j)
       if (src[j] >= 0) s += v[j];
-    if (y_f32) {
-      reinterpret_cast<f32x4*>(static_cast<float*>(y) + static_cast<size_t>(t) * H)[c] = s;
+    if (y_mode != kYBF16) {
+      f32x4* yo = reinterpret_cast<f32x4*>(static_cast<float*>(y) + static_cast<size_t>(t) * H) + c;
+      if (y_mode == kYF32Add) s = *yo + s;
+      *yo = s;
     } else {
       const uint32_t lo = f32_to_bf16(s[0]) | (static_cast<uint32_t>(f32_to_bf16(s[1])) << 16);
       const uint32_t hi = f32_to_bf16(s[2]) | (static_cast<uint32_t>(f32_to_bf16(s[3])) << 16);
@@ -145,7 +149,7 @@ __global__ __launch_bounds__(kCThreads) void residual_prenorm_kernel(uint16_t* _
 }  // namespace
 
 hipError_t launch_combine(const float* rows, const int32_t* inv, int T, int k, int H, void* y,
-                          int y_f32, hipStream_t stream) {
+                          int y_mode, hipStream_t stream) {
   if (T <= 0) return hipSuccess;
   // small batches: one column block per workgroup (a single round of loads);
   // large batches: one workgroup per token
@@ -155,7 +159,7 @@ hipError_t launch_combine(const float* rows, const int32_t* inv, int T, int k, i
 #define MOE_COMBINE_K(KK)                                                                       \
   case KK:                                                                                      \
     hipLaunchKernelGGL(combine_kernel<KK>, grid, dim3(kCThreads), 0, stream, rows, inv, H, y, \
-                       y_f32);                                                                  \
+                       y_mode);                                                                 \
     break;
     MOE_COMBINE_K(1) MOE_COMBINE_K(2) MOE_COMBINE_K(3) MOE_COMBINE_K(4)
     MOE_COMBINE_K(5) MOE_COMBINE_K(6) MOE_COMBINE_K(7) MOE_COMBINE_K(8)

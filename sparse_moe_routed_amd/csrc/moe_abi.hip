@@ -36,6 +36,22 @@ moe_status dims_check(const moe_dims* d) {
 
 bool dims_ok(const moe_dims* d) { return dims_check(d) == MOE_OK; }
 
+// the shared expert: one expert (E = 1) that every token takes (k = 1)
+moe_status shared_dims_check(const moe_dims* d) {
+  if (!d) return MOE_EINVAL;
+  if (d->hidden <= 0 || d->ffn <= 0 || d->n_experts != 1 || d->top_k != 1) return MOE_EINVAL;
+  if (d->hidden % 64 || d->ffn % 64) return MOE_EUNSUPPORTED;
+  return MOE_OK;
+}
+
+// an expert bank to pack: any expert count, layer widths as dims_check
+moe_status bank_dims_check(const moe_dims* d) {
+  if (!d) return MOE_EINVAL;
+  if (d->hidden <= 0 || d->ffn <= 0 || d->n_experts <= 0) return MOE_EINVAL;
+  if (d->hidden % 64 || d->ffn % 64 || d->n_experts > 256) return MOE_EUNSUPPORTED;
+  return MOE_OK;
+}
+
 bool fmt_ok(int32_t fmt) { return fmt == kBF16 || fmt == kFP8 || fmt == kNVFP4; }
 
 bool aligned(const void* p, uintptr_t n) { return reinterpret_cast<uintptr_t>(p) % n == 0; }
@@ -306,11 +322,15 @@ struct StageMarks {
 // The forward pass.  With `cc` set, the expert weights come from the cache:
 // after the permutation the row counts go to the host, the missing experts
 // are uploaded into slots, and the GEMMs read the slots through slot_of.
+// With `shared`, the one expert of dims (E = 1, k = 1) takes every token with
+// weight 1 (no ids or gates); with `accumulate`, the result is added to the
+// fp32 values y holds.
 int32_t forward_impl(const moe_dims* dims, int32_t T, const void* x, const int32_t* ids,
                      const float* gates, const moe_experts* ex_in, void* y, int32_t y_dtype,
                      void* ws, size_t ws_bytes, void* stream, void* const* events,
-                     int32_t n_events, const CacheCall* cc = nullptr) {
-  if (const moe_status ds = dims_check(dims)) return ds;
+                     int32_t n_events, const CacheCall* cc = nullptr, bool shared = false,
+                     bool accumulate = false) {
+  if (const moe_status ds = shared ? shared_dims_check(dims) : dims_check(dims)) return ds;
   moe_experts cached_bank{};
   const moe_experts* ex = ex_in;
   if (cc) {
@@ -335,8 +355,10 @@ int32_t forward_impl(const moe_dims* dims, int32_t T, const void* x, const int32
   if (T < 0 || T > kMaxTokens) return MOE_EINVAL;
   if (!fmt_ok(ex->fmt)) return MOE_EINVAL;
   if (y_dtype != MOE_Y_BF16 && y_dtype != MOE_Y_F32) return MOE_EINVAL;
+  if (accumulate && y_dtype != MOE_Y_F32) return MOE_EINVAL;
   if (T == 0) return MOE_OK;  // nothing is read or written; pointers may be null
-  if (!x || !ids || !gates || !y || !ex->up || !ex->down) return MOE_EINVAL;
+  if (!x || !y || !ex->up || !ex->down) return MOE_EINVAL;
+  if (!shared && (!ids || !gates)) return MOE_EINVAL;
   if (ex->fmt != kBF16 && (!ex->up_s || !ex->down_s)) return MOE_EINVAL;
   if (ex->fmt == kNVFP4 && (!ex->up_bs || !ex->down_bs)) return MOE_EINVAL;
   if (!aligned(x, 16) || !aligned(y, 16) || !aligned(ids, 4) || !aligned(gates, 4) ||
@@ -372,7 +394,8 @@ int32_t forward_impl(const moe_dims* dims, int32_t T, const void* x, const int32
   p.zero_words = amax_x;  // amax slots of x and of the intermediate
   p.n_zero = 2 * moe::kAmaxSlots;
   marks.mark(0);
-  hipError_t err = moe::launch_permute(ids, gates, T, E, k, p, st);
+  hipError_t err = shared ? moe::launch_permute_identity(R, p, st)
+                          : moe::launch_permute(ids, gates, T, E, k, p, st);
   if (err != hipSuccess) return MOE_EHIP;
 
   // 1b. cached weights: bring the experts this batch touches into slots
@@ -515,8 +538,8 @@ int32_t forward_impl(const moe_dims* dims, int32_t T, const void* x, const int32
 
   // 6. combine
   marks.mark(5);
-  err = moe::launch_combine(at<float>(ws, L.out_rows), p.inv, T, k, H, y, y_dtype == MOE_Y_F32,
-                            st);
+  const int y_mode = accumulate ? moe::kYF32Add : (y_dtype == MOE_Y_F32 ? moe::kYF32 : moe::kYBF16);
+  err = moe::launch_combine(at<float>(ws, L.out_rows), p.inv, T, k, H, y, y_mode, st);
   marks.mark(6);
   return hip_status(err);
 }
@@ -540,6 +563,21 @@ int32_t moe_forward_timed(const moe_dims* dims, int32_t T, const void* x, const 
                       n_events);
 }
 
+size_t moe_shared_workspace_size(const moe_dims* dims, int32_t fmt, int32_t max_tokens) {
+  if (shared_dims_check(dims) != MOE_OK || !fmt_ok(fmt) || max_tokens < 0 ||
+      max_tokens > kMaxTokens)
+    return 0;
+  return make_layout(dims, fmt, max_tokens).total;
+}
+
+int32_t moe_shared_forward(const moe_dims* dims, int32_t T, const void* x,
+                           const moe_experts* expert, void* y, int32_t y_dtype, int32_t accumulate,
+                           void* ws, size_t ws_bytes, void* stream) {
+  if (accumulate != 0 && accumulate != 1) return MOE_EINVAL;
+  return forward_impl(dims, T, x, nullptr, nullptr, expert, y, y_dtype, ws, ws_bytes, stream,
+                      nullptr, 0, nullptr, true, accumulate == 1);
+}
+
 int32_t moe_forward_cached(const moe_dims* dims, int32_t T, const void* x, const int32_t* ids,
                            const float* gates, const moe_cache* cache, void* state, void* y,
                            int32_t y_dtype, void* ws, size_t ws_bytes, void* stream,
@@ -552,7 +590,7 @@ int32_t moe_forward_cached(const moe_dims* dims, int32_t T, const void* x, const
 int32_t moe_quantize_experts(const moe_dims* dims, int32_t fmt, const void* up_bf16,
                              const void* down_bf16, void* up_q, void* down_q, uint8_t* up_bs,
                              uint8_t* down_bs, float* up_s, float* down_s, void* stream) {
-  if (const moe_status ds = dims_check(dims)) return ds;
+  if (const moe_status ds = bank_dims_check(dims)) return ds;
   if (fmt != kFP8 && fmt != kNVFP4) return MOE_EINVAL;
   if (!up_bf16 || !down_bf16 || !up_q || !down_q || !up_s || !down_s) return MOE_EINVAL;
   if (fmt == kNVFP4 && (!up_bs || !down_bs)) return MOE_EINVAL;

@@ -58,6 +58,9 @@ hipError_t launch_router(const uint16_t* x, const uint16_t* w_packed, const floa
 
 hipError_t launch_permute(const int32_t* ids, const float* gates, int T, int E, int k,
                           const PermBufs& p, hipStream_t stream);
+// One expert taking every token with weight 1 (the shared expert): the
+// permutation is the identity, written without ids or gates.
+hipError_t launch_permute_identity(int T, const PermBufs& p, hipStream_t stream);
 
 // Grouped GEMM over the tile list.  Up: out = bf16(relu(scale * A_g W^T)^2)
 // with A_g the token rows gathered through sorted_src; down:
@@ -116,8 +119,10 @@ hipError_t launch_quant_nvfp4(const uint16_t* x, const int32_t* n_rows_dev, int 
                               uint8_t* bs, float* scale, hipStream_t stream);
 hipError_t launch_zero_u32(uint32_t* p, int n, hipStream_t stream);
 
+// output modes of the combine: bf16 y, fp32 y, fp32 y += the combined rows
+enum YMode { kYBF16 = 0, kYF32 = 1, kYF32Add = 2 };
 hipError_t launch_combine(const float* rows, const int32_t* inv, int T, int k, int H, void* y,
-                          int y_f32, hipStream_t stream);
+                          int y_mode, hipStream_t stream);
 
 // Per-tensor quantisation of a whole bf16 tensor [rows, cols] (the tokens,
 // or moe_quantize_activation): amax into the zeroed slots `amax`, then codes

@@ -223,7 +223,43 @@ __global__ __launch_bounds__(kPermThreads) void perm_single_kernel(
   scatter_chunk(ev, gates, R, E, 0, cnt, wcnt, sorted_src, inv, row_gate);
 }
 
+// The identity permutation of one expert that takes all R rows with gate
+// 1: row i is flat entry i.  Workgroup 0 also writes the counts, offsets and
+// tile prefixes and clears the accumulation words.
+__global__ __launch_bounds__(kPermThreads) void perm_identity_kernel(
+    int R, int32_t* __restrict__ counts, int32_t* __restrict__ offsets, int bm0,
+    int32_t* __restrict__ tile_off0, int bm1, int32_t* __restrict__ tile_off1,
+    uint32_t* __restrict__ zero_words, int n_zero, int32_t* __restrict__ sorted_src,
+    int32_t* __restrict__ inv, float* __restrict__ row_gate) {
+  for (int i = blockIdx.x * kPermThreads + threadIdx.x; i < R; i += gridDim.x * kPermThreads) {
+    sorted_src[i] = i;
+    inv[i] = i;
+    row_gate[i] = 1.0f;
+  }
+  if (blockIdx.x == 0) {
+    for (int i = threadIdx.x; i < n_zero; i += kPermThreads) zero_words[i] = 0u;
+    if (threadIdx.x == 0) {
+      counts[0] = R;
+      offsets[0] = 0;
+      offsets[1] = R;
+      tile_off0[0] = 0;
+      tile_off0[1] = (R + bm0 - 1) / bm0;
+      tile_off1[0] = 0;
+      tile_off1[1] = (R + bm1 - 1) / bm1;
+    }
+  }
+}
+
 }  // namespace
+
+hipError_t launch_permute_identity(int R, const PermBufs& p, hipStream_t stream) {
+  int g = (R + kPermThreads - 1) / kPermThreads;
+  g = g < 1 ? 1 : (g > 1024 ? 1024 : g);
+  hipLaunchKernelGGL(perm_identity_kernel, dim3(g), dim3(kPermThreads), 0, stream, R, p.counts,
+                     p.offsets, p.bm0, p.tile_off0, p.bm1, p.tile_off1, p.zero_words, p.n_zero,
+                     p.sorted_src, p.inv, p.row_gate);
+  return hipGetLastError();
+}
 
 hipError_t launch_permute(const int32_t* ids, const float* gates, int T, int E, int k,
                           const PermBufs& p, hipStream_t stream) {

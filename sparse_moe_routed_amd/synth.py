@@ -20,6 +20,9 @@ Recipe (all PCG64 `numpy.random.default_rng`):
   tokens x        bf16(rng(4000+T).standard_normal((T, H), f32))
   outlier rows    rng(5000+T).choice(T, round(0.1*T), replace=False), x4
                   (exact in bf16: a power-of-two scale)
+  shared expert   rng(3500+l): W_up = bf16(std_normal((F_s, H)) / sqrt(H)),
+                  W_down = bf16(std_normal((H, F_s)) / sqrt(F_s)), F_s = 3712
+                  (assumed: the pages give no shared-expert width)
 bf16 conversion is round-to-nearest-even (torch's `.to(torch.bfloat16)`).
 """
 from __future__ import annotations
@@ -37,6 +40,10 @@ FFN = 1856
 N_EXPERTS = 128
 TOP_K = 6
 N_MOE_LAYERS = 23
+# Width of the shared expert beside the routed ones.  The pages keep shared
+# experts on the card but give no width; two routed-expert widths is an
+# assumption of this build, not a fact from them.
+SHARED_FFN = 2 * FFN
 
 
 @dataclass(frozen=True)
@@ -96,6 +103,15 @@ def make_experts(layer: int = 0, dims: Dims = Dims(), experts=None):
     with ThreadPoolExecutor(_threads()) as ex:
         list(ex.map(fill, range(len(ids))))
     return up, down
+
+
+def make_shared_expert(layer: int = 0, hidden: int = HIDDEN, ffn: int = SHARED_FFN):
+    """bf16 shared expert W_up [F_s, H] and W_down [H, F_s] (torch CPU), drawn
+    like a routed expert from rng(3500 + layer)."""
+    rng = np.random.default_rng(3500 + layer)
+    up = rng.standard_normal((ffn, hidden), dtype=np.float32) / np.float32(math.sqrt(hidden))
+    down = rng.standard_normal((hidden, ffn), dtype=np.float32) / np.float32(math.sqrt(ffn))
+    return _to_bf16(up), _to_bf16(down)
 
 
 def outlier_rows(T: int) -> np.ndarray:

@@ -174,6 +174,34 @@ def test_forward_validation(lib):
                                  1, FAKE, need, None, None, moe.N_TIMED_EVENTS) == moe.EINVAL
 
 
+def test_shared_validation(lib):
+    sd = moe.Dims(2688, 3712, 1, 1)
+    need = lib.moe_shared_workspace_size(ctypes.byref(sd), 0, 64)
+    assert need > 0 and need % 256 == 0
+    assert lib.moe_shared_workspace_size(ctypes.byref(_dims()), 0, 64) == 0  # not one expert
+    assert lib.moe_shared_workspace_size(ctypes.byref(moe.Dims(2688, 3700, 1, 1)), 0, 64) == 0
+    ex = moe.Experts(0, FAKE.value, FAKE.value, None, None, None, None)
+
+    def call(dims=sd, T=64, x=FAKE, e=ex, y=FAKE, yd=1, acc=0, ws=FAKE, wsb=need):
+        return lib.moe_shared_forward(ctypes.byref(dims), T, x, e if e is None else ctypes.byref(e),
+                                      y, yd, acc, ws, wsb, None)
+
+    assert call(dims=_dims()) == moe.EINVAL
+    assert call(dims=moe.Dims(2688, 3712, 1, 2)) == moe.EINVAL
+    assert call(dims=moe.Dims(2688, 3700, 1, 1)) == moe.EUNSUPPORTED
+    assert call(e=None) == moe.EINVAL
+    assert call(x=None) == moe.EINVAL
+    assert call(y=None) == moe.EINVAL
+    assert call(acc=2) == moe.EINVAL
+    assert call(acc=1, yd=0) == moe.EINVAL  # accumulating needs fp32 y
+    assert call(x=ctypes.c_void_p(FAKE.value + 8)) == moe.EINVAL
+    assert call(wsb=need - 1) == moe.EWORKSPACE
+    assert call(T=0, x=None, ws=None, wsb=0) == moe.OK
+    # a one-expert bank can be packed (top_k is not used there)
+    assert lib.moe_quantize_experts(ctypes.byref(sd), 1, None, FAKE, FAKE, FAKE, None, None, FAKE,
+                                    FAKE, None) == moe.EINVAL
+
+
 def test_cache_validation(lib):
     d = _dims()
     assert lib.moe_cache_state_size(ctypes.byref(d), 5) == 0    # fewer slots than top_k
