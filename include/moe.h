@@ -53,7 +53,7 @@
 extern "C" {
 #endif
 
-#define MOE_ABI_VERSION 6
+#define MOE_ABI_VERSION 7
 
 typedef enum {
   MOE_OK = 0,
@@ -220,6 +220,26 @@ size_t moe_shared_workspace_size(const moe_dims* dims, int32_t fmt, int32_t max_
 int32_t moe_shared_forward(const moe_dims* dims, int32_t T, const void* x,
                            const moe_experts* expert, void* y, int32_t y_dtype,
                            int32_t accumulate, void* ws, size_t ws_bytes, void* stream);
+
+/* moe_forward for callers that cannot allocate device memory: code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc.  It
+ * takes no workspace: scratch lives in a fixed device array inside the
+ * library, MOE_NOALLOC_SCRATCH_BYTES per GPU, which each GPU the library runs
+ * on holds until the process ends (8 MiB: up to 64 tokens at the full layer
+ * shape in every format).  The call allocates nothing and calls no
+ * allocating routine.  Arguments, results and errors are those of
+ * moe_forward, plus:
+ *   MOE_EWORKSPACE  moe_workspace_size(dims, fmt, T) exceeds the array
+ *   MOE_EINVAL      `stream` belongs to a device other than the current one
+ * The array is found on the current device (hipGetDevice) the first time the
+ * call runs there.  Every call on one GPU shares that GPU's array, which keeps
+ * the last call's stage results: calls that may overlap on one GPU (other
+ * streams, other threads) race, so order them on one stream. */
+#define MOE_NOALLOC_SCRATCH_BYTES (8u << 20)
+int32_t moe_forward_noalloc(const moe_dims* dims, int32_t T, const void* x,
+                            const int32_t* ids, const float* gates,
+                            const moe_experts* experts, void* y, int32_t y_dtype,
+                            void* stream);
 
 /* ---- expert residency split
  * The routed expert banks stay in host memory in their stored format; the

@@ -94,6 +94,9 @@ _SIGS = {
                                             ctypes.POINTER(Experts), ctypes.c_void_p, ctypes.c_int32,
                                             ctypes.c_int32, ctypes.c_void_p, ctypes.c_size_t,
                                             ctypes.c_void_p]),
+    "moe_forward_noalloc": (ctypes.c_int32, [ctypes.POINTER(Dims), ctypes.c_int32, ctypes.c_void_p,
+                                             ctypes.c_void_p, ctypes.c_void_p, ctypes.POINTER(Experts),
+                                             ctypes.c_void_p, ctypes.c_int32, ctypes.c_void_p]),
     "moe_cache_state_size": (ctypes.c_size_t, [ctypes.POINTER(Dims), ctypes.c_int32]),
     "moe_cache_init": (ctypes.c_int32, [ctypes.POINTER(Dims), ctypes.POINTER(Cache), ctypes.c_void_p,
                                         ctypes.c_size_t, ctypes.c_void_p]),
@@ -119,7 +122,7 @@ _SIGS = {
 }
 
 _lib = None
-ABI_VERSION = 6  # MOE_ABI_VERSION of include/moe.h this binding describes
+ABI_VERSION = 7  # MOE_ABI_VERSION of include/moe.h this binding describes
 
 
 def lib():
@@ -327,6 +330,30 @@ def shared_forward(x: torch.Tensor, expert: ExpertBank, dims: LayerDims,
     _check("moe_shared_forward", lib().moe_shared_forward(
         ctypes.byref(d), T, _ptr(x), ctypes.byref(e), _ptr(y), yd, int(bool(accumulate)),
         _ptr(ws), ws.numel(), _stream()))
+    return y
+
+
+NOALLOC_SCRATCH_BYTES = 8 << 20  # MOE_NOALLOC_SCRATCH_BYTES of include/moe.h
+
+
+def forward_noalloc(x: torch.Tensor, ids: torch.Tensor, gates: torch.Tensor, experts: ExpertBank,
+                    dims: LayerDims = LayerDims(), y_dtype: torch.dtype = torch.float32,
+                    y: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """moe_forward_noalloc: moe_forward with the library's fixed device
+    scratch instead of a workspace (y is allocated here unless passed)."""
+    T = x.shape[0]
+    _dev(x, torch.bfloat16, "x", (T, dims.hidden))
+    _dev(ids, torch.int32, "ids", (T, dims.top_k))
+    _dev(gates, torch.float32, "gates", (T, dims.top_k))
+    if y is None:
+        y = torch.empty((T, dims.hidden), dtype=y_dtype, device=x.device)
+    _dev(y, y_dtype, "y", (T, dims.hidden))
+    yd = {torch.float32: Y_F32, torch.bfloat16: Y_BF16}[y_dtype]
+    d = dims.c()
+    e = experts.c()
+    _check("moe_forward_noalloc", lib().moe_forward_noalloc(
+        ctypes.byref(d), T, _ptr(x), _ptr(ids), _ptr(gates), ctypes.byref(e), _ptr(y), yd,
+        _stream()))
     return y
 
 

@@ -6,6 +6,7 @@
 
 #include <algorithm>
 #include <limits>
+#include <mutex>
 
 #include "../../include/moe.h"
 
@@ -187,6 +188,30 @@ struct CacheCall {
   void* state;
   moe_cache_stats* stats;
 };
+
+// ---- fixed device scratch of moe_forward_noalloc.  Every GPU the library
+// runs on holds its own copy of this array until the process ends.  In host
+// code `scratch` only names the symbol: the device address of the current
+// device's copy comes from hipGetSymbolAddress, looked up once per device and
+// kept in scratch_at[]; kernels receive that address, never the array's name.
+constexpr size_t kNoallocScratch = MOE_NOALLOC_SCRATCH_BYTES;
+constexpr int kMaxDevices = 64;
+static __device__ __align__(256) uint8_t scratch[kNoallocScratch];
+std::mutex scratch_mu;
+void* scratch_at[kMaxDevices];
+
+// device address of `scratch` on device `dev`, which must be current
+moe_status scratch_for(int dev, void** out) {
+  if (dev < 0 || dev >= kMaxDevices) return MOE_EUNSUPPORTED;
+  std::lock_guard<std::mutex> lock(scratch_mu);
+  if (!scratch_at[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return MOE_EHIP;
+    scratch_at[dev] = p;
+  }
+  *out = scratch_at[dev];
+  return MOE_OK;
+}
 
 }  // namespace
 
@@ -576,6 +601,27 @@ int32_t moe_shared_forward(const moe_dims* dims, int32_t T, const void* x,
   if (accumulate != 0 && accumulate != 1) return MOE_EINVAL;
   return forward_impl(dims, T, x, nullptr, nullptr, expert, y, y_dtype, ws, ws_bytes, stream,
                       nullptr, 0, nullptr, true, accumulate == 1);
+}
+
+int32_t moe_forward_noalloc(const moe_dims* dims, int32_t T, const void* x, const int32_t* ids,
+                            const float* gates, const moe_experts* ex, void* y, int32_t y_dtype,
+                            void* stream) {
+  if (const moe_status ds = dims_check(dims)) return ds;
+  if (!ex || T < 0 || T > kMaxTokens || !fmt_ok(ex->fmt)) return MOE_EINVAL;
+  if (T == 0)  // validates the rest; nothing is enqueued
+    return forward_impl(dims, T, x, ids, gates, ex, y, y_dtype, nullptr, 0, stream, nullptr, 0);
+  if (make_layout(dims, ex->fmt, T).total > kNoallocScratch) return MOE_EWORKSPACE;
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess) return MOE_EHIP;
+  if (stream) {
+    hipDevice_t sd = -1;
+    if (hipStreamGetDevice(static_cast<hipStream_t>(stream), &sd) != hipSuccess) return MOE_EHIP;
+    if (sd != dev) return MOE_EINVAL;  // the stream's device must be the current one
+  }
+  void* ws = nullptr;
+  if (const moe_status ss = scratch_for(dev, &ws)) return ss;
+  return forward_impl(dims, T, x, ids, gates, ex, y, y_dtype, ws, kNoallocScratch, stream, nullptr,
+                      0);
 }
 
 int32_t moe_forward_cached(const moe_dims* dims, int32_t T, const void* x, const int32_t* ids,

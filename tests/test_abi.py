@@ -202,6 +202,23 @@ def test_shared_validation(lib):
                                     FAKE, None) == moe.EINVAL
 
 
+def test_noalloc_validation(lib):
+    d = _dims()
+    ex = moe.Experts(0, FAKE.value, FAKE.value, None, None, None, None)
+
+    def call(T=4, e=ex, x=FAKE):
+        return lib.moe_forward_noalloc(ctypes.byref(d), T, x, FAKE, FAKE,
+                                       e if e is None else ctypes.byref(e), FAKE, 1, None)
+
+    assert call(e=None) == moe.EINVAL
+    assert call(T=-1) == moe.EINVAL
+    assert call(e=moe.Experts(7, FAKE.value, FAKE.value, None, None, None, None)) == moe.EINVAL
+    # a batch whose workspace exceeds the fixed scratch is refused before any HIP call
+    assert lib.moe_workspace_size(ctypes.byref(d), 0, 4096) > moe.NOALLOC_SCRATCH_BYTES
+    assert call(T=4096) == moe.EWORKSPACE
+    assert call(T=0, x=None) == moe.OK
+
+
 def test_cache_validation(lib):
     d = _dims()
     assert lib.moe_cache_state_size(ctypes.byref(d), 5) == 0    # fewer slots than top_k
