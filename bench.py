@@ -61,6 +61,10 @@ def parse():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-prefill", action="store_true",
                    help="skip the 4096-token prefill record of a decode workload")
+    p.add_argument("--shared", type=int, default=0, metavar="F_S",
+                   help="time the MoE block: each layer adds a shared expert of this width "
+                        "(moe_shared_forward accumulating into the routed y; 3712 is the "
+                        "assumed width)")
     p.add_argument("--graph", action="store_true",
                    help="also capture one step into a HIP graph and time K replays "
                         "(reported beside the eager headline)")
@@ -199,7 +203,22 @@ def build_layers(fmt, n_layers, dev, ld, verbose=True):
     return layers
 
 
-def measure(args, name, layers, hip):
+def build_shared(fmt, n_layers, f_s, dev):
+    """Shared expert of each layer on the device (seeded synthetic), or None."""
+    import sparse_moe_routed_amd as moe
+    from sparse_moe_routed_amd import synth
+
+    if not f_s:
+        return None
+    sd = moe.shared_dims(synth.HIDDEN, f_s)
+    out = []
+    for l in range(n_layers):
+        up, down = synth.make_shared_expert(l, ffn=f_s)
+        out.append(moe.quantize_experts(up[None].to(dev), down[None].to(dev), fmt, sd))
+    return sd, out
+
+
+def measure(args, name, layers, hip, shared=None):
     """Time one workload (see the module docstring).  Returns (record, state):
     the record of the bench line without its headline keys, and the device
     tensors of the last step for the parity check."""
@@ -223,12 +242,16 @@ def measure(args, name, layers, hip):
     gates = torch.empty((T, k), dtype=torch.float32, device=dev)
     xin = torch.empty_like(x0)
     xs = x0.clone()
+    sws = None
+    if shared:
+        sws = moe.shared_workspace(shared[0], fmt, T, dev)
     torch.cuda.synchronize()
     stream = torch.cuda.current_stream().cuda_stream
     n_ev = moe.N_TIMED_EVENTS
 
-    def run_layer(L, x_in, ev=None):
-        """route + forward of one layer; ev = (route events, stage events) or None"""
+    def run_layer(L, x_in, ev=None, li=0):
+        """route + forward of one layer (+ the shared expert added into y);
+        ev = (route events, stage events) or None"""
         if ev:
             hip.record(ev[0][0], stream)
         moe.route(x_in, L["router"], ld, ids=ids, gates=gates, ws=rws)
@@ -237,6 +260,8 @@ def measure(args, name, layers, hip):
             moe.forward_timed(x_in, ids, gates, L["bank"], ev[1], ld, ws=ws, y=y)
         else:
             moe.forward(x_in, ids, gates, L["bank"], ld, ws=ws, y=y)
+        if shared:
+            moe.shared_forward(x_in, shared[1][li], shared[0], y=y, accumulate=True, ws=sws)
 
     def step(evs=None):
         if n_layers == 1:
@@ -247,7 +272,7 @@ def measure(args, name, layers, hip):
             xs.copy_(x0)
             moe.prenorm(xs, xin)
             for li, L in enumerate(layers):
-                run_layer(L, xin, evs[li] if evs else None)
+                run_layer(L, xin, evs[li] if evs else None, li)
                 if li + 1 < n_layers:
                     moe.residual_prenorm(xs, y, xin)
                 else:
@@ -391,7 +416,8 @@ def measure(args, name, layers, hip):
         "ms_per_step": round(ms_per_step, 4),
         "dtype": fmt,
         "config": {"workload": name, "T": T, "hidden": H, "ffn": F, "experts": E,
-                   "top_k": k, "format": fmt, "layers": n_layers, "outlier_rows": wl["outliers"]},
+                   "top_k": k, "format": fmt, "layers": n_layers, "outlier_rows": wl["outliers"],
+                   "shared_ffn": shared[0].ffn if shared else 0},
         "layer_hbm_gbs": round(layer_bytes / (layer_ms * 1e-3) / 1e9, 1),
         "layer_tflops": round(2 * flops_up / (layer_ms * 1e-3) / 1e12, 2),
         "experts_touched": touched,
@@ -444,7 +470,8 @@ def main():
     ld = moe.LayerDims()
 
     layers = build_layers(fmt, n_layers, dev, ld)
-    rec, state = measure(args, args.workload, layers, hip)
+    shared = build_shared(fmt, n_layers, args.shared, dev)
+    rec, state = measure(args, args.workload, layers, hip, shared)
     out = {
         "metric": METRIC,
         "value": rec.pop("value"),
@@ -463,7 +490,7 @@ def main():
     out.update(rec)
     if not args.no_cpu_baseline:
         out["cpu_baseline"], out["parity"] = cpu_baseline(args.workload, state)
-        if n_layers > 1:
+        if n_layers > 1 or shared:
             # the timed step ends with the last layer's output; per-layer
             # parity of the stack is a GPU test (teacher-forced)
             out["parity"] = None
@@ -471,7 +498,7 @@ def main():
     # the MFMA half of the metric: the 4096-token prefill batch of the same
     # format, with the same layer weights
     pre = f"prefill_t4096_{fmt}"
-    if (not args.no_prefill and n_layers == 1 and wl["T"] < 4096 and pre in synth.WORKLOADS
+    if (not args.no_prefill and not shared and n_layers == 1 and wl["T"] < 4096 and pre in synth.WORKLOADS
             and synth.WORKLOADS[pre]["layers"] == 1):
         del state
         torch.cuda.empty_cache()
