@@ -1005,8 +1005,11 @@ __global__ __launch_bounds__(NW * 64) void grouped_gemm_nv_kernel(GemmArgs g) {
   // weights; its loads per step are then QA, not QA + 2, and the waits below
   // count exactly the loads issued (an unused load left to the compiler would
   // be removed and the count would be off).
-  auto issue = [&](int step_in, uint8_t* buf, auto& codes, auto& scales, auto ml_c) {
+  // NT: weights with the non-temporal cache policy (a weight panel that only
+  // this workgroup reads, as in the kernels above).
+  auto issue = [&](int step_in, uint8_t* buf, auto& codes, auto& scales, auto ml_c, auto nt_c) {
     constexpr int ML = decltype(ml_c)::value;
+    constexpr bool NT = decltype(nt_c)::value;
     const int step = min(step_in, n_steps - 1);
     const int kb = step * 128;
 #pragma unroll
@@ -1016,8 +1019,16 @@ __global__ __launch_bounds__(NW * 64) void grouped_gemm_nv_kernel(GemmArgs g) {
                                        16, 0, 0);
     }
     if constexpr (ML > 0) {
-      codes = *reinterpret_cast<const u32x4*>(b_code + static_cast<size_t>(step) * code_step);
-      scales = *reinterpret_cast<const uint32_t*>(b_scale + static_cast<size_t>(step) * scale_step);
+      const u32x4* pc = reinterpret_cast<const u32x4*>(b_code + static_cast<size_t>(step) * code_step);
+      const uint32_t* ps =
+          reinterpret_cast<const uint32_t*>(b_scale + static_cast<size_t>(step) * scale_step);
+      if constexpr (NT) {
+        codes = __builtin_nontemporal_load(pc);
+        scales = __builtin_nontemporal_load(ps);
+      } else {
+        codes = *pc;
+        scales = *ps;
+      }
     }
   };
 
@@ -1077,37 +1088,48 @@ __global__ __launch_bounds__(NW * 64) void grouped_gemm_nv_kernel(GemmArgs g) {
   // LDS, weights into the ring), meet, start the loads NBUF - 1 steps ahead
   // into the buffer and ring slot everyone finished with, multiply
   uint8_t* const bufs[4] = {lds0, lds1, lds2, lds3};
-  auto body = [&](int step, auto j_c, auto ml_c) {
+  auto body = [&](int step, auto j_c, auto ml_c, auto nt_c) {
     constexpr int J = decltype(j_c)::value;
     constexpr int AHEAD = (J + NBUF - 1) % NBUF;
     constexpr int DPS = QA + (decltype(ml_c)::value > 0 ? 2 : 0);  // loads per step
     __builtin_amdgcn_s_waitcnt(vmcnt_imm((NBUF - 2) * DPS));
     __asm__ volatile("s_barrier" ::: "memory");
-    issue(step + NBUF - 1, bufs[AHEAD], bc[AHEAD], bsc[AHEAD], ml_c);
+    issue(step + NBUF - 1, bufs[AHEAD], bc[AHEAD], bsc[AHEAD], ml_c, nt_c);
     if (step < n_steps) compute(bufs[J], bc[J], bsc[J], ml_c);
   };
   using I0 = std::integral_constant<int, 0>;
   using I1 = std::integral_constant<int, 1>;
   using I2 = std::integral_constant<int, 2>;
   using I3 = std::integral_constant<int, 3>;
-  auto main_loop = [&](auto ml_c) {
-    issue(0, lds0, bc[0], bsc[0], ml_c);
-    if constexpr (NBUF >= 3) issue(1, lds1, bc[1], bsc[1], ml_c);
-    if constexpr (NBUF >= 4) issue(2, lds2, bc[2], bsc[2], ml_c);
+  auto main_loop = [&](auto ml_c, auto nt_c) {
+    issue(0, lds0, bc[0], bsc[0], ml_c, nt_c);
+    if constexpr (NBUF >= 3) issue(1, lds1, bc[1], bsc[1], ml_c, nt_c);
+    if constexpr (NBUF >= 4) issue(2, lds2, bc[2], bsc[2], ml_c, nt_c);
     for (int step0 = 0; step0 < n_steps; step0 += NBUF) {
-      body(step0, I0{}, ml_c);
-      body(step0 + 1, I1{}, ml_c);
-      if constexpr (NBUF >= 3) body(step0 + 2, I2{}, ml_c);
-      if constexpr (NBUF >= 4) body(step0 + 3, I3{}, ml_c);
+      body(step0, I0{}, ml_c, nt_c);
+      body(step0 + 1, I1{}, ml_c, nt_c);
+      if constexpr (NBUF >= 3) body(step0 + 2, I2{}, ml_c, nt_c);
+      if constexpr (NBUF >= 4) body(step0 + 3, I3{}, ml_c, nt_c);
     }
     __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
   };
-  switch (ml) {
-    case 0: main_loop(std::integral_constant<int, 0>{}); break;
-    case 1: main_loop(std::integral_constant<int, (MB >= 1 ? 1 : MB)>{}); break;
-    case 2: main_loop(std::integral_constant<int, (MB >= 2 ? 2 : MB)>{}); break;
-    case 3: main_loop(std::integral_constant<int, (MB >= 3 ? 3 : MB)>{}); break;
-    default: main_loop(std::integral_constant<int, MB>{}); break;
+  auto run = [&](auto nt_c) {
+    switch (ml) {
+      case 0: main_loop(std::integral_constant<int, 0>{}, nt_c); break;
+      case 1: main_loop(std::integral_constant<int, (MB >= 1 ? 1 : MB)>{}, nt_c); break;
+      case 2: main_loop(std::integral_constant<int, (MB >= 2 ? 2 : MB)>{}, nt_c); break;
+      case 3: main_loop(std::integral_constant<int, (MB >= 3 ? 3 : MB)>{}, nt_c); break;
+      default: main_loop(std::integral_constant<int, MB>{}, nt_c); break;
+    }
+  };
+  // decode tiles: non-temporal weight loads when this workgroup is the
+  // panel's only reader (the expert has one row tile); prefill tiles keep one
+  // code path
+  if constexpr (BM <= 32) {
+    if (te == 1) run(std::true_type{});
+    else run(std::false_type{});
+  } else {
+    run(std::false_type{});
   }
 
   // ---- epilogue (as in the kernels above, one wave row)
@@ -1223,6 +1245,12 @@ struct PrefillTile<kNVFP4, 1> {
 constexpr int kDecodeRows = 32;
 constexpr int kDecodeMaxT = 512;
 constexpr int kDecodeBuffers = 3;
+// NVFP4 decode tiles run in grouped_gemm_nv_kernel (weights straight into
+// registers, non-temporal for single-tile experts) with 4 activation buffers:
+// T = 64 up 60.4 -> 53.3 us, down 56.5 -> 52.1 us against the direct-load
+// kernel; T = 4 up 21.3 -> 18.1 us, down 16.1 -> 13.9 us (3 buffers: 19.8 /
+// 15.8 us at T = 4, equal at T = 64; 2 buffers: equal at T = 64).
+constexpr int kNvDecodeBuffers = 4;
 
 // Below this many tokens the up projection touches so few experts that its
 // workgroups cannot be spread evenly over the CUs (about 2.3 per CU at four
@@ -1235,6 +1263,9 @@ constexpr int kNarrowUpMaxT = 16;
 
 template <int FMT, int STAGE>
 hipError_t launch_fmt_stage(int T, const GemmArgs& g, hipStream_t stream, const KernelEvents& ev) {
+  if constexpr (FMT == kNVFP4) {
+    if (T < kDecodeMaxT) return launch_nv<STAGE, kDecodeRows, 4, kNvDecodeBuffers>(g, stream, ev);
+  }
   if constexpr (FMT == kNVFP4 || FMT == kFP8) {
     if (T < kDecodeMaxT)
       return launch_dma<FMT, STAGE, kDecodeRows, 128, 1, 4, kDecodeBuffers>(g, stream, ev);
