@@ -194,13 +194,19 @@ __global__ __launch_bounds__(WM* WN * 64) void grouped_gemm_kernel(GemmArgs g) {
   u32x4 b_reg[kPrefetch][B_CH];
   u32x4 bp_reg[2][B_PCH];
 
-  // Loads are issued unconditionally (no branches around vector memory ops,
-  // so the compiler can wait for exactly the set it needs): steps past the end
-  // re-read the last step.  K is a multiple of 64, so bf16 rows hold whole
+  // BF16: steps past the end are not loaded (a wave-uniform branch).
+  // Re-reading the last step there cost 2-7 % of a decode launch: the
+  // non-temporal weight lines are not kept for a second read.  Expanded FP8
+  // codes: steps past the end re-read the last step (no branches around the
+  // loads; a branch there made the compiler wait for more than the set it
+  // needs, 5-25 % slower).  K is a multiple of 64, so bf16 rows hold whole
   // 128-byte steps.
   auto load = [&](int step_in, auto set_c, auto nt_c) __attribute__((always_inline)) {
     constexpr int SET = decltype(set_c)::value;
     constexpr bool NT = decltype(nt_c)::value;
+    if constexpr (FMT == kBF16) {
+      if (step_in >= n_steps) return;
+    }
     const int step = min(step_in, n_steps - 1);
     const int kb = step * kStepBytes;
 #pragma unroll
@@ -342,8 +348,8 @@ __global__ __launch_bounds__(WM* WN * 64) void grouped_gemm_kernel(GemmArgs g) {
 
   // ---- main loop: one barrier per K step, double-buffered LDS, loads two
   // steps ahead in two register sets.  Unrolled by two so register sets are
-  // compile-time indices; a trailing iteration past the last step stores and
-  // loads (clamped) but does not compute.
+  // compile-time indices; a trailing iteration past the last step stores
+  // into a buffer that is not read again and computes nothing.
   using S0 = std::integral_constant<int, 0>;
   using S1 = std::integral_constant<int, 1>;
   auto main_loop = [&](auto ml_c, auto nt_c) __attribute__((always_inline)) {
