@@ -399,6 +399,15 @@ def test_forward_quantised_full_shape(full, fmt, T):
     _forward_case(full, fmt, T, explain=True)
 
 
+@pytest.mark.parametrize("fmt", ["bf16", "fp8", "nvfp4"])
+@pytest.mark.parametrize("T", [8, 128])
+def test_forward_two_token_verify_batches(full, fmt, T):
+    # multi-token-prediction verification feeds two positions per sequence
+    # (cortiq model card, "Usage"): 4 and 64 sequences (SGLang-Omni
+    # cookbook, "Serve a checkpoint": 64 running requests), every element
+    _forward_case(full, fmt, T, explain=fmt != "bf16")
+
+
 @pytest.mark.parametrize("outliers", [False, True])
 @pytest.mark.parametrize("fmt", ["fp8", "nvfp4"])
 def test_forward_quantised_prefill_t4096(full, fmt, outliers):
