@@ -8,18 +8,24 @@
 //
 // A workgroup computes a BM x BN tile of one expert: BM sorted rows of that
 // expert (row tiles counted by the permutation on the device) times BN output
-// columns.  Both operands are K-contiguous.  Two kernels:
+// columns.  Both operands are K-contiguous.  Four kernels:
 //   grouped_gemm_kernel (BF16 and FP8 up-projection decode batches, 32-row
 //     tiles): weight streaming; each thread loads 16-byte chunks two K steps
 //     ahead into registers and stores them into double-buffered LDS (rows
 //     padded to 144 bytes); FP8 up-projection codes are expanded on the way
 //     into LDS.
-//   grouped_gemm_dma_kernel (prefill, 128-row tiles, and NVFP4 and FP8
-//     down-projection decode, 32-row tiles): operands go from global memory
-//     straight into LDS
-//     (global_load_lds_dwordx4) as stored, into an XOR-swizzled layout; weight
-//     codes are expanded per lane when the MFMA fragments are formed.  See
-//     the comment above that kernel.
+//   grouped_gemm_rk_kernel (BF16 decode of a single expert whose grid is too
+//     small to fill the chip: the shared expert): K split over the waves of
+//     a workgroup, operands straight into registers, partial sums added
+//     through LDS.
+//   grouped_gemm_dma_kernel (BF16 and FP8 prefill, 128-row tiles, and the
+//     FP8 down projection at decode, 32-row tiles): operands go from global
+//     memory straight into LDS (global_load_lds_dwordx4) as stored, into an
+//     XOR-swizzled layout; weight codes are expanded per lane when the MFMA
+//     fragments are formed.  See the comment above that kernel.
+//   grouped_gemm_nv_kernel (NVFP4, decode and prefill): packed weight codes
+//     and block scales go from the panel layout straight into registers,
+//     activations through LDS.
 // Formats:
 //   BF16 : v_mfma_f32_32x32x16_bf16, 64 K per step.
 //   FP8  : v_mfma_scale_f32_32x32x64_f8f6f4 with unit E8M0 scales (E4M3 x
@@ -250,9 +256,16 @@ __global__ __launch_bounds__(WM* WN * 64) void grouped_gemm_kernel(GemmArgs g) {
       outw[2 * w] = __builtin_bit_cast(uint32_t, lo);
       outw[2 * w + 1] = __builtin_bit_cast(uint32_t, hi);
     }
+    // Lanes 4-7 of each group of eight write a row 32 rows below lanes 0-3,
+    // which sits on the same LDS banks (32 rows of 144 bytes are a multiple
+    // of the bank period).  They write their 32 bytes in the other order, so
+    // each store instruction's eight lanes cover distinct banks (bank
+    // conflicts 88 % of LDS cycles -> 0).
     u32x4* dst = reinterpret_cast<u32x4*>(dst_b);
-    dst[0] = u32x4{outw[0], outw[1], outw[2], outw[3]};
-    dst[1] = u32x4{outw[4], outw[5], outw[6], outw[7]};
+    const u32x4 first = u32x4{outw[0], outw[1], outw[2], outw[3]};
+    const u32x4 second = u32x4{outw[4], outw[5], outw[6], outw[7]};
+    dst[h0] = h0 ? second : first;
+    dst[h0 ^ 1] = h0 ? first : second;
   };
 
   // the half HS (0: even step, 1: odd step) of pair set PS into buffer buf
@@ -476,6 +489,154 @@ __global__ __launch_bounds__(WM* WN * 64) void grouped_gemm_kernel(GemmArgs g) {
     }
   }
   if constexpr (STAGE == 0 && FMT != kBF16) block_amax_to_slots(local_max, g.amax);
+}
+
+// ---------------------------------------------------------------------------
+// BF16 decode kernel for grids too small to fill the chip (one expert, a few
+// row tiles: the shared expert at decode).  The kernels above give each
+// workgroup a whole K loop, so a grid of a few dozen workgroups keeps a few
+// dozen waves' loads in flight.  Here a workgroup of KS waves computes one
+// 32 x 32 tile and wave w takes the K steps w, w + KS, w + 2 KS, ...: KS
+// times more waves stream the same weights.  Both operands go straight into
+// registers (a ring of P steps of loads in flight per wave; no LDS and no
+// barrier in the K loop), and the waves' fp32 partial sums are added through
+// LDS in wave order at the end, so results do not depend on timing.
+//
+// A step is 64 K: sub-step q multiplies K 16 q .. 16 q + 15, the lane half
+// lk supplying its 8 values at 16 q + 8 lk (the MFMA's own K order), so one
+// load instruction reads 32 contiguous bytes of each of 32 rows.  Ordinary
+// loads: with the non-temporal policy each line was dropped before the next
+// instruction read its other bytes, at half the speed.
+template <int STAGE, int KS, int P>
+__global__ __launch_bounds__(KS * 64) void grouped_gemm_rk_kernel(GemmArgs g) {
+  static_assert(KS >= 1 && KS <= 8 && P >= 1 && P <= 4, "split and depth");
+  constexpr int BM = 32, BN = 32;
+  __shared__ f32x4 part[KS > 1 ? (KS - 1) * 4 * 64 : 1];
+
+  // ---- which tile (same order as the kernels above)
+  const int n_ntiles = (g.N + BN - 1) / BN;
+  const int total = g.tile_off[g.E] * n_ntiles;
+  const int per_xcd = (total + 7) >> 3;
+  const int local = blockIdx.x >> 3;
+  if (local >= per_xcd) return;
+  const int logical = (blockIdx.x & 7) * per_xcd + local;
+  if (logical >= total) return;
+  const int e = owner_expert(g.tile_off, g.E, n_ntiles, logical);
+  const int te = g.tile_off[e + 1] - g.tile_off[e];
+  const int loc = logical - g.tile_off[e] * n_ntiles;
+  const int ntile = loc / te;
+  const int mt = loc - ntile * te;
+  const int row0 = g.offsets[e] + mt * BM;
+  const int rows_valid = min(BM, g.offsets[e + 1] - row0);
+  const int n0 = ntile * BN;
+  const int ew = g.w_slot ? g.w_slot[e] : e;
+
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int lrow = lane & 31, lk = lane >> 5;
+  const int K = g.K, N = g.N;
+  const size_t row_bytes = static_cast<size_t>(K) * 2;
+  const int n_steps = K / 64;  // K is a multiple of 64
+  // this wave's steps; a wave with none (K shorter than KS steps) adds zeros
+  const int n_my = n_steps > wave ? (n_steps - wave + KS - 1) / KS : 0;
+
+  // rows past the tile's last one read that row again, columns past N the
+  // last column; both are masked in the epilogue
+  const int rr = min(lrow, rows_valid - 1);
+  size_t src;
+  if constexpr (STAGE == 0) {
+    src = static_cast<size_t>(g.sorted_src[row0 + rr] / g.top_k);
+  } else {
+    src = static_cast<size_t>(row0 + rr);
+  }
+  const int n = min(n0 + lrow, N - 1);
+  const uint8_t* a_ptr = static_cast<const uint8_t*>(g.a) + src * row_bytes + wave * 128 + lk * 16;
+  const uint8_t* b_ptr = static_cast<const uint8_t*>(g.b) +
+                         (static_cast<size_t>(ew) * N + n) * row_bytes + wave * 128 + lk * 16;
+  constexpr int kStride = KS * 128;  // bytes between a wave's consecutive steps
+
+  u32x4 ra[P][4], rb[P][4];
+  f32x16 acc;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) acc[r] = 0.f;
+
+  // the wave's step j into ring slot SLOT
+  auto load = [&](int j, auto slot_c) __attribute__((always_inline)) {
+    constexpr int SLOT = decltype(slot_c)::value;
+    const size_t off = static_cast<size_t>(j) * kStride;
+    const u32x4* pa = reinterpret_cast<const u32x4*>(a_ptr + off);
+    const u32x4* pb = reinterpret_cast<const u32x4*>(b_ptr + off);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      ra[SLOT][q] = pa[2 * q];
+      rb[SLOT][q] = pb[2 * q];
+    }
+  };
+  auto compute = [&](auto slot_c) __attribute__((always_inline)) {
+    constexpr int SLOT = decltype(slot_c)::value;
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, ra[SLOT][q]),
+                                                    __builtin_bit_cast(bf16x8, rb[SLOT][q]), acc,
+                                                    0, 0, 0);
+  };
+  // steps j0 .. j0 + P - 1 from the ring, each slot refilled P steps ahead
+  // (no loads past the wave's last step)
+  auto prime = [&](auto slot_c) __attribute__((always_inline)) {
+    if (decltype(slot_c)::value < n_my) load(decltype(slot_c)::value, slot_c);
+  };
+  prime(std::integral_constant<int, 0>{});
+  if constexpr (P >= 2) prime(std::integral_constant<int, 1>{});
+  if constexpr (P >= 3) prime(std::integral_constant<int, 2>{});
+  if constexpr (P >= 4) prime(std::integral_constant<int, 3>{});
+  for (int j0 = 0; j0 < n_my; j0 += P) {
+    auto one = [&](auto slot_c) __attribute__((always_inline)) {
+      constexpr int SLOT = decltype(slot_c)::value;
+      const int j = j0 + SLOT;
+      if (j < n_my) compute(slot_c);
+      if (j + P < n_my) load(j + P, slot_c);
+    };
+    one(std::integral_constant<int, 0>{});
+    if constexpr (P >= 2) one(std::integral_constant<int, 1>{});
+    if constexpr (P >= 3) one(std::integral_constant<int, 2>{});
+    if constexpr (P >= 4) one(std::integral_constant<int, 3>{});
+  }
+
+  // ---- partial sums of waves 1 .. KS - 1 through LDS, added in wave order
+  if constexpr (KS > 1) {
+    if (wave > 0) {
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+        part[((wave - 1) * 4 + q) * 64 + lane] =
+            f32x4{acc[4 * q], acc[4 * q + 1], acc[4 * q + 2], acc[4 * q + 3]};
+    }
+    __syncthreads();
+    if (wave > 0) return;
+#pragma unroll
+    for (int w = 0; w < KS - 1; ++w)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const f32x4 v = part[(w * 4 + q) * 64 + lane];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) acc[4 * q + i] += v[i];
+      }
+  }
+
+  // ---- epilogue (wave 0).  Lane holds column lane % 32 and rows
+  // 8 (r / 4) + 4 (lane / 32) + r % 4.
+  const int col = n0 + lrow;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    const int rl = (r >> 2) * 8 + lk * 4 + (r & 3);
+    if (rl < rows_valid && col < N) {
+      const size_t at = static_cast<size_t>(row0 + rl) * N + col;
+      if constexpr (STAGE == 0) {
+        static_cast<uint16_t*>(g.out)[at] = relu_sq_bf16(acc[r]);
+      } else {
+        static_cast<float*>(g.out)[at] = acc[r] * g.row_gate[row0 + rl];
+      }
+    }
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -1216,6 +1377,15 @@ hipError_t launch_one(const GemmArgs& g, hipStream_t stream, const KernelEvents&
 }
 
 
+template <int STAGE, int KS, int P>
+hipError_t launch_rk(const GemmArgs& g, hipStream_t stream, const KernelEvents& ev) {
+  const int n_ntiles = (g.N + 31) / 32;
+  long long blocks = static_cast<long long>(g.max_tiles) * n_ntiles;
+  blocks = (blocks + 7) / 8 * 8;
+  return dispatch(reinterpret_cast<const void*>(&grouped_gemm_rk_kernel<STAGE, KS, P>), blocks,
+                  KS * 64, g, stream, ev);
+}
+
 // Prefill tile of each format and projection (rows x columns, waves in M x N,
 // LDS buffers), chosen by measurement on the 4096-token batch: 128 x 128
 // tiles with eight 64 x 32 wave tiles and two buffers (two workgroups per CU)
@@ -1267,6 +1437,20 @@ constexpr int kNvDecodeBuffers = 4;
 // is fastest with 128 columns).
 constexpr int kNarrowUpMaxT = 16;
 
+// BF16 decode of a single expert (the shared expert) over fewer 128-column
+// tiles than this runs in the split-K kernel, 4 waves per 32 x 32 tile with
+// 3 steps in flight each.  Shared expert of width 3712 in a BF16 block step:
+// T = 64 0.359 -> 0.346 ms, T = 4 0.137 -> 0.110 ms (8 waves per tile, or 2
+// or 4 steps in flight, measured within 1 % of this).  Routed batches keep
+// the kernels above.
+constexpr int kSmallGridTiles = 256;
+constexpr int kSplitK = 4;
+constexpr int kSplitDepth = 3;
+inline bool small_decode_grid(const GemmArgs& g) {
+  return g.E == 1 &&
+         static_cast<long long>(g.max_tiles) * ((g.N + 127) / 128) < kSmallGridTiles;
+}
+
 template <int FMT, int STAGE>
 hipError_t launch_fmt_stage(int T, const GemmArgs& g, hipStream_t stream, const KernelEvents& ev) {
   if constexpr (FMT == kNVFP4) {
@@ -1276,6 +1460,10 @@ hipError_t launch_fmt_stage(int T, const GemmArgs& g, hipStream_t stream, const 
     if (T < kDecodeMaxT)
       return launch_dma<FMT, STAGE, kDecodeRows, 128, 1, 4, kDecodeBuffers>(g, stream, ev);
   } else {
+    if constexpr (FMT == kBF16) {
+      if (T < kDecodeMaxT && small_decode_grid(g))
+        return launch_rk<STAGE, kSplitK, kSplitDepth>(g, stream, ev);
+    }
     if (STAGE == 0 && T < kNarrowUpMaxT) {
       if constexpr (FMT == kBF16)
         return launch_one<FMT, STAGE, kDecodeRows, 32, 1, 1>(g, stream, ev);
