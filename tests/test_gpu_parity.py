@@ -496,6 +496,22 @@ def test_shared_expert_matches_oracle(shared, fmt, T):
     assert err <= TOL[fmt]
 
 
+@pytest.mark.parametrize("T", [200, 256])
+def test_shared_expert_split_k_boundary(shared, T):
+    # BF16 single-expert decode, width 3712: at 200 tokens both projections
+    # run the split-K kernel (7 row tiles, the last one 8 rows); at 256 the
+    # up projection (9 row tiles x 29 column tiles of 128) is past its grid
+    # limit and runs the LDS-staged kernel, the down projection (9 x 21)
+    # still the split-K one; every element
+    x = _x(T, FULL, outliers=True)
+    y = moe.shared_forward(x.cuda(), shared["bank"]("bf16"), shared["dims"])
+    torch.cuda.synchronize()
+    y_ref = om.shared_expert(x.float().numpy(), shared["up"], shared["down"], "bf16")
+    err, rms = _rel_err(y.cpu().double().numpy(), y_ref)
+    _log(f"shared bf16 T={T}: max|d|/rms = {err:.3e} (rms {rms:.3f})")
+    assert err <= TOL["bf16"]
+
+
 def test_shared_expert_prefill_t4096_bf16(shared):
     # the dense 4096-token batch with outlier rows, every element
     x = _x(4096, FULL, outliers=True)
