@@ -904,10 +904,13 @@ __global__ __launch_bounds__(WM* WN * 64) void grouped_gemm_dma_kernel(GemmArgs 
     constexpr int ML = decltype(ml_c)::value;
     if constexpr (ML > 0) {
       if constexpr (FMT == kFP8) {
-        // the second 64-byte half of the last step lies past K when K % 128 == 64
+        // the second 64-byte half of the last step lies past K when K % 128 ==
+        // 64: that half is skipped (its products would all be zero, and an
+        // accumulator that starts at +0 stays unchanged by adding +0)
         const bool tail = (step * 128 + 64 >= a_bytes);
 #pragma unroll
         for (int s = 0; s < 2; ++s) {  // 64 K per MFMA: chunks 4s + 2lk, +1
+          if (s == 1 && tail) break;
           i32x8 af[ML], bfr[NB];
           const int c0 = s * 4 + lk * 2;
 #pragma unroll
@@ -923,11 +926,6 @@ __global__ __launch_bounds__(WM* WN * 64) void grouped_gemm_dma_kernel(GemmArgs 
             const u32x4 x1 = *reinterpret_cast<const u32x4*>(buf + b_row[j] + (((c0 + 1) ^ b_sw[j]) << 4));
             bfr[j] = i32x8{(int)x0[0], (int)x0[1], (int)x0[2], (int)x0[3],
                            (int)x1[0], (int)x1[1], (int)x1[2], (int)x1[3]};
-            if (s == 1 && tail) bfr[j] = i32x8{0, 0, 0, 0, 0, 0, 0, 0};
-          }
-          if (s == 1 && tail) {
-#pragma unroll
-            for (int i = 0; i < ML; ++i) af[i] = i32x8{0, 0, 0, 0, 0, 0, 0, 0};
           }
 #pragma unroll
           for (int i = 0; i < ML; ++i)
