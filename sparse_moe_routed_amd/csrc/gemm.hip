@@ -95,8 +95,8 @@ __global__ __launch_bounds__(WM* WN * 64) void grouped_gemm_kernel(GemmArgs g) {
   constexpr int NT = WM * WN * 64;
   constexpr int WTM = BM / WM, WTN = BN / WN;  // wave tile
   constexpr int MB = WTM / 32, NB = WTN / 32;  // 32x32 MFMA blocks per wave
-  // NVFP4 and the FP8 down projection (fp8 MFMA) run in
-  // grouped_gemm_dma_kernel at every size.
+  // the FP8 down projection (fp8 MFMA) runs in grouped_gemm_dma_kernel and
+  // NVFP4 in grouped_gemm_nv_kernel at every size
   static_assert(FMT == kBF16 || FMT == kFP8X, "BF16 and expanded FP8 only");
   // 16-byte source chunks per step: A rows 8 each, bf16 B rows 8 each (FP8
   // codes are loaded per pair of steps, below).  When a tile has fewer chunks
@@ -644,13 +644,13 @@ __global__ __launch_bounds__(KS * 64) void grouped_gemm_rk_kernel(GemmArgs g) {
 // Per-thread ds_write staging costs about as much LDS time as all the
 // fragment reads of a K step on this part; direct loads move each 16-byte
 // chunk from L1 into LDS without passing through VGPRs.  Operands are staged
-// as stored: bf16 / fp16 / E4M3 activations, and bf16, E4M3 or packed E2M1
-// weight codes (with their E4M3 block scales); codes are expanded per lane
-// when the MFMA fragments are formed.
+// as stored: bf16 / E4M3 activations and bf16 weights or E4M3 weight codes;
+// codes of the up projection are expanded per lane when the MFMA fragments
+// are formed.
 //
-// LDS holds NBUF buffers of one K step: BM activation rows of 128 bytes, BN
-// weight rows of RB bytes (128 bf16 / fp8, 64 fp8 codes expanded to bf16, 32
-// packed E2M1), and for NVFP4 BN rows of 4 block-scale bytes.  Rows are not
+// LDS holds NBUF buffers of one K step: BM activation rows of 128 bytes and
+// BN weight rows of RB bytes (128 bf16 / fp8, 64 fp8 codes expanded to
+// bf16).  Rows are not
 // padded: chunk c (16 bytes) of row r sits in slot c ^ ((r / (256 / RB)) %
 // (RB / 16)), so the 16 rows that a quarter-wave ds_read_b128 touches at one
 // chunk land on distinct banks.  A direct load writes one wave's 64 x 16
@@ -660,7 +660,7 @@ __global__ __launch_bounds__(KS * 64) void grouped_gemm_rk_kernel(GemmArgs g) {
 // meets at a barrier, after which every wave's loads are visible.
 //
 // K order inside a step: BF16 and FP8 feed the MFMA in natural order.  For
-// the expanded formats lane half lk takes the step's K range [32 lk, 32 lk +
+// expanded FP8 codes lane half lk takes the step's K range [32 lk, 32 lk +
 // 32) and sub-step s its 8 values at 32 lk + 8 s, so one lane's codes are
 // contiguous; activations are read in the same order (a permutation of K
 // inside the step, which the exact products and fp32 sums do not notice
@@ -678,21 +678,20 @@ constexpr int vmcnt_imm(int n) { return (n & 15) | (7 << 4) | (15 << 8) | ((n >>
 template <int FMT, int STAGE, int BM, int BN, int WM, int WN, int NBUF>
 __global__ __launch_bounds__(WM* WN * 64) void grouped_gemm_dma_kernel(GemmArgs g) {
   static_assert(NBUF >= 2 && NBUF <= 4, "buffers");
+  static_assert(FMT == kBF16 || FMT == kFP8 || FMT == kFP8X, "bf16, fp8 or expanded fp8");
   constexpr int NW = WM * WN;
   constexpr int WTM = BM / WM, WTN = BN / WN;
   constexpr int MB = WTM / 32, NB = WTN / 32;
-  constexpr bool EXPAND = (FMT == kFP8X || FMT == kNVFP4);
+  constexpr bool EXPAND = FMT == kFP8X;
   constexpr int AESZ = (FMT == kFP8) ? 1 : 2;           // activation bytes per element
   constexpr int KS = 128 / AESZ;                         // K elements per step
-  constexpr int RB = (FMT == kFP8X) ? 64 : (FMT == kNVFP4 ? 32 : 128);  // weight row bytes per step
-  constexpr int WB = (FMT == kNVFP4) ? 2 : 1;            // weight codes: 1/WB bytes per element
+  constexpr int RB = (FMT == kFP8X) ? 64 : 128;          // weight row bytes per step
   constexpr int NA = BM / 8;                             // activation loads per step (8 rows each)
   constexpr int NBL = BN * RB / 1024;                    // weight loads per step
-  constexpr int NSC = (FMT == kNVFP4) ? BN / 64 : 0;     // scale loads per step (4 bytes x 64 rows)
-  constexpr int QA = (NA + NW - 1) / NW, QB = (NBL + NW - 1) / NW, QS = (NSC + NW - 1) / NW;
-  constexpr int DPS = QA + QB + QS;                      // vector memory operations per wave per step
-  constexpr int A_OFF = 0, B_OFF = BM * 128, S_OFF = BM * 128 + BN * RB;
-  constexpr int BUF = S_OFF + (FMT == kNVFP4 ? BN * 4 : 0);
+  constexpr int QA = (NA + NW - 1) / NW, QB = (NBL + NW - 1) / NW;
+  constexpr int DPS = QA + QB;                           // vector memory operations per wave per step
+  constexpr int A_OFF = 0, B_OFF = BM * 128;
+  constexpr int BUF = BM * 128 + BN * RB;
   static_assert(NA * 8 == BM && NBL * 1024 == BN * RB && BM % 16 == 0 && BN % 64 == 0, "tile");
   __shared__ __attribute__((aligned(1024))) uint8_t lds0[BUF];
   __shared__ __attribute__((aligned(1024))) uint8_t lds1[BUF];
@@ -722,7 +721,7 @@ __global__ __launch_bounds__(WM* WN * 64) void grouped_gemm_dma_kernel(GemmArgs 
   const int wm = wave / WN, wn = wave % WN;
   const int K = g.K, N = g.N;
   const int a_bytes = K * AESZ;                 // activation row bytes
-  const int w_bytes = (FMT == kBF16) ? 2 * K : K / WB;  // weight row bytes
+  const int w_bytes = (FMT == kBF16) ? 2 * K : K;       // weight row bytes
   const int n_steps = (K + KS - 1) / KS;
 
   // ---- per-lane global sources of the direct loads (fixed over K).  When a
@@ -747,13 +746,13 @@ __global__ __launch_bounds__(WM* WN * 64) void grouped_gemm_dma_kernel(GemmArgs 
     a_cof[q] = c * 16;
   }
   constexpr int CPR = RB / 16;  // 16-byte chunks per weight row and step
-  // NVFP4 and FP8 (down projection) weights sit in panels stored
+  // FP8 down-projection codes sit in panels stored
   // K-step-major (the tile lies inside one panel): a step of the tile's rows
   // is contiguous, w_step bytes apart.  FP8 steps are whole 128-byte lines;
   // when K % 128 == 64 the last step holds 64 bytes per row, and its chunks
   // move by b_tail[q] (chunks past K re-read the row's in-range chunk 64
   // bytes earlier and are zeroed when the fragments are formed).
-  constexpr bool kPanels = FMT == kNVFP4 || FMT == kFP8;
+  constexpr bool kPanels = FMT == kFP8;
   static_assert(!kPanels || kNvPanel % BN == 0, "panel-layout tiles stay inside one panel");
   static_assert(FMT != kFP8 || RB == kFp8StepK, "fp8 panel steps");
   const int nv_pn0 = n0 - n0 % kNvPanel;
@@ -776,17 +775,6 @@ __global__ __launch_bounds__(WM* WN * 64) void grouped_gemm_dma_kernel(GemmArgs 
     }
     b_dst[q] = B_OFF + qi * 1024;
     b_tail[q] = -((n - nv_pn0) * (RB / 2) + (c & (CPR / 2)) * 16);
-  }
-  const uint8_t* s_src[QS > 0 ? QS : 1];
-  int s_dst[QS > 0 ? QS : 1];
-  if constexpr (QS > 0) {
-#pragma unroll
-    for (int q = 0; q < QS; ++q) {
-      const int qi = (wave + q * NW) % NSC;
-      const int n = min(n0 + qi * 64 + lane, N - 1);
-      s_src[q] = g.b_bs + (static_cast<size_t>(ew) * N + nv_pn0) * (K / 16) + (n - nv_pn0) * 4;
-      s_dst[q] = S_OFF + qi * 256;
-    }
   }
 
   // issue the direct loads of one K step into buffer buf.  Steps past the end
@@ -815,13 +803,6 @@ __global__ __launch_bounds__(WM* WN * 64) void grouped_gemm_dma_kernel(GemmArgs 
       __builtin_amdgcn_global_load_lds(p, (__attribute__((address_space(3))) void*)(buf + b_dst[q]),
                                        16, 0, kWeightPolicy);
     }
-    if constexpr (QS > 0) {
-#pragma unroll
-      for (int q = 0; q < QS; ++q)
-        __builtin_amdgcn_global_load_lds(s_src[q] + step * (nv_rows * 4),
-                                         (__attribute__((address_space(3))) void*)(buf + s_dst[q]),
-                                         4, 0, 0);
-    }
   };
 
   // row blocks dealt to wave rows in turn (as in grouped_gemm_kernel).  A
@@ -847,7 +828,7 @@ __global__ __launch_bounds__(WM* WN * 64) void grouped_gemm_dma_kernel(GemmArgs 
   const int lrow = lane & 31;
   const int lk = lane >> 5;
   // byte offsets of this lane's rows inside a buffer, and their swizzles
-  int a_row[MB], a_sw[MB], b_row[NB], b_sw[NB], s_row[NB];
+  int a_row[MB], a_sw[MB], b_row[NB], b_sw[NB];
 #pragma unroll
   for (int i = 0; i < MB; ++i) {
     const int r = (i * WM + wm) * 32 + lrow;
@@ -859,11 +840,10 @@ __global__ __launch_bounds__(WM* WN * 64) void grouped_gemm_dma_kernel(GemmArgs 
     const int r = wn * WTN + j * 32 + lrow;
     b_row[j] = B_OFF + r * RB;
     b_sw[j] = lds_swz<RB>(r);
-    s_row[j] = S_OFF + r * 4;
   }
 
-  using frag = std::conditional_t<FMT == kNVFP4, f16x8, bf16x8>;
-  // weight fragments of one lane for the 4 sub-steps of a step (expanded formats)
+  using frag = bf16x8;
+  // weight fragments of one lane for the 4 sub-steps of a step (expanded FP8)
   auto weight_frags = [&](const uint8_t* buf, int j, frag (&out)[4]) {
     if constexpr (FMT == kFP8X) {
       // 32 E4M3 codes at K 32 lk .. 32 lk + 31 -> bf16 (unit scale: exact)
@@ -877,25 +857,6 @@ __global__ __launch_bounds__(WM* WN * 64) void grouped_gemm_dma_kernel(GemmArgs 
         const bf16x2 p2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w[2 * s + 1], 1.0f, false);
         const bf16x2 p3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w[2 * s + 1], 1.0f, true);
         out[s] = bf16x8{p0[0], p0[1], p1[0], p1[1], p2[0], p2[1], p3[0], p3[1]};
-      }
-    } else if constexpr (FMT == kNVFP4) {
-      // 32 E2M1 codes at K 32 lk .. 32 lk + 31 (element 2i in the low nibble)
-      // -> fp16 (unit scale), times their E4M3 block scales (exact in fp16)
-      const u32x4 x = *reinterpret_cast<const u32x4*>(buf + b_row[j] + ((lk ^ b_sw[j]) << 4));
-      // the lane's two block scales (bytes 2 lk, 2 lk + 1 of the row's four);
-      // every E4M3 value is exact in fp16
-      const uint32_t sc4 = *reinterpret_cast<const uint32_t*>(buf + s_row[j]);
-      const f16x2 scs = lk ? __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(sc4, 1.0f, true)
-                           : __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(sc4, 1.0f, false);
-#pragma unroll
-      for (int s = 0; s < 4; ++s) {
-        const _Float16 sc = s < 2 ? scs[0] : scs[1];
-        const f16x2 s2 = {sc, sc};
-        const f16x2 p0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(x[s], 1.0f, 0) * s2;
-        const f16x2 p1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(x[s], 1.0f, 1) * s2;
-        const f16x2 p2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(x[s], 1.0f, 2) * s2;
-        const f16x2 p3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(x[s], 1.0f, 3) * s2;
-        out[s] = f16x8{p0[0], p0[1], p1[0], p1[1], p2[0], p2[1], p3[0], p3[1]};
       }
     }
   };
@@ -948,12 +909,8 @@ __global__ __launch_bounds__(WM* WN * 64) void grouped_gemm_dma_kernel(GemmArgs 
 #pragma unroll
           for (int i = 0; i < ML; ++i)
 #pragma unroll
-            for (int j = 0; j < NB; ++j) {
-              if constexpr (FMT == kNVFP4)
-                acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af[i], bx[j][s], acc[i][j], 0, 0, 0);
-              else
-                acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bx[j][s], acc[i][j], 0, 0, 0);
-            }
+            for (int j = 0; j < NB; ++j)
+              acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bx[j][s], acc[i][j], 0, 0, 0);
         }
       } else {
 #pragma unroll
@@ -1075,8 +1032,9 @@ __global__ __launch_bounds__(WM* WN * 64) void grouped_gemm_dma_kernel(GemmArgs 
 }
 
 // ---------------------------------------------------------------------------
-// NVFP4 prefill kernel: weights straight into registers, activations through
-// LDS.  In the bank's panel layout one K step (64 elements) of 32 consecutive
+// NVFP4 kernel (prefill and decode): weights straight into registers,
+// activations through LDS.  In the bank's panel layout one K step (64
+// elements) of 32 consecutive
 // weight rows is 1 KB of codes and 128 bytes of block scales, contiguous, and
 // exactly what one wave's MFMA fragments need: lane l takes row l % 32, codes
 // of K [32 (l / 32), + 32) (16 bytes) and the row's 4 block scales.  So each
@@ -1413,9 +1371,8 @@ struct PrefillTile<kNVFP4, 1> {
 
 // decode batches: 32-row tiles, in the register-staged kernel (BF16, and the
 // FP8 up projection with its codes expanded on the way into LDS) or the
-// direct-load kernel with three LDS buffers (NVFP4: packed codes in LDS take
-// a quarter of the expanded fp16 bytes; the FP8 down projection: 2-3 % faster
-// than register staging at 4 and 64 tokens)
+// direct-load kernel with three LDS buffers (the FP8 down projection: 2-3 %
+// faster than register staging at 4 and 64 tokens)
 constexpr int kDecodeRows = 32;
 constexpr int kDecodeMaxT = 512;
 constexpr int kDecodeBuffers = 3;
@@ -1451,28 +1408,27 @@ inline bool small_decode_grid(const GemmArgs& g) {
 
 template <int FMT, int STAGE>
 hipError_t launch_fmt_stage(int T, const GemmArgs& g, hipStream_t stream, const KernelEvents& ev) {
+  const bool decode = T < kDecodeMaxT;
   if constexpr (FMT == kNVFP4) {
-    if (T < kDecodeMaxT) return launch_nv<STAGE, kDecodeRows, 4, kNvDecodeBuffers>(g, stream, ev);
-  }
-  if constexpr (FMT == kNVFP4 || FMT == kFP8) {
-    if (T < kDecodeMaxT)
-      return launch_dma<FMT, STAGE, kDecodeRows, 128, 1, 4, kDecodeBuffers>(g, stream, ev);
-  } else {
-    if constexpr (FMT == kBF16) {
-      if (T < kDecodeMaxT && small_decode_grid(g))
-        return launch_rk<STAGE, kSplitK, kSplitDepth>(g, stream, ev);
-    }
-    if (STAGE == 0 && T < kNarrowUpMaxT) {
-      if constexpr (FMT == kBF16)
-        return launch_one<FMT, STAGE, kDecodeRows, 32, 1, 1>(g, stream, ev);
-      return launch_one<FMT, STAGE, kDecodeRows, 64, 1, 2>(g, stream, ev);
-    }
-    if (T < kDecodeMaxT) return launch_one<FMT, STAGE, kDecodeRows, 128, 1, 4>(g, stream, ev);
-  }
-  if constexpr (FMT == kNVFP4) {
+    if (decode) return launch_nv<STAGE, kDecodeRows, 4, kNvDecodeBuffers>(g, stream, ev);
     using P = PrefillTile<FMT, STAGE>;
     return launch_nv<STAGE, P::BM, P::WN, P::NBUF>(g, stream, ev);
   } else {
+    if constexpr (FMT == kFP8) {
+      if (decode)
+        return launch_dma<FMT, STAGE, kDecodeRows, 128, 1, 4, kDecodeBuffers>(g, stream, ev);
+    } else {
+      if constexpr (FMT == kBF16) {
+        if (decode && small_decode_grid(g))
+          return launch_rk<STAGE, kSplitK, kSplitDepth>(g, stream, ev);
+      }
+      if (STAGE == 0 && T < kNarrowUpMaxT) {
+        if constexpr (FMT == kBF16)
+          return launch_one<FMT, STAGE, kDecodeRows, 32, 1, 1>(g, stream, ev);
+        return launch_one<FMT, STAGE, kDecodeRows, 64, 1, 2>(g, stream, ev);
+      }
+      if (decode) return launch_one<FMT, STAGE, kDecodeRows, 128, 1, 4>(g, stream, ev);
+    }
     using P = PrefillTile<FMT, STAGE>;
     return launch_dma<FMT, STAGE, P::BM, P::BN, P::WM, P::WN, P::NBUF>(g, stream, ev);
   }
