@@ -379,33 +379,56 @@ def measure(args, name, layers, hip, shared=None):
     touched = int(np.unique(ids_h).size)
     R = T * k
     wbe = weight_bytes_per_expert(fmt, F, H)
-    act_in_bytes = {"bf16": 2, "fp8": 1, "nvfp4": 2}[fmt]
     layer_bytes = touched * 2 * wbe + E * H * 4 + E * 4 + T * H * 2 + T * H * 4
     flops_up = 2.0 * R * F * H
     dom = "up" if gemm_kernel_ms["up"] >= gemm_kernel_ms["down"] else "down"
     dur_s = gemm_kernel_ms[dom] * 1e-3
+    # algorithmic bytes of the dominant launch: the touched experts' weights
+    # once, its activation input once, its output once (FP8 up projections
+    # read the tokens as bf16 values of their codes, FP8 down projections read
+    # E4M3 codes, NVFP4 reads fp16 values)
+    a_in = {"bf16": 2, "fp8": 2 if dom == "up" else 1, "nvfp4": 2}[fmt]
+    if dom == "up":
+        alg = touched * wbe + T * H * a_in + R * F * 2
+    else:
+        alg = touched * wbe + R * F * a_in + R * H * 4
+    hbm_gbs = alg / dur_s / 1e9
     if T <= 256:
-        # weight-streaming launch: bytes of the touched experts' panels plus
-        # its activation input and output
-        if dom == "up":
-            alg = touched * wbe + T * H * act_in_bytes + R * F * 2
-        else:
-            alg = touched * wbe + R * F * act_in_bytes + R * H * 4
-        achieved = alg / dur_s / 1e9
-        roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
-                "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+        # weight-streaming launch
+        roof = {"bound": "hbm", "achieved": round(hbm_gbs, 1), "peak": HBM_PEAK_GBS,
+                "unit": "GB/s", "frac": round(hbm_gbs / HBM_PEAK_GBS, 4),
                 "traffic": None, "kernel": f"grouped_gemm_{dom}", "alg_bytes": int(alg)}
     else:
-        achieved = flops_up / dur_s / 1e12
-        peak = MFMA_PEAK_TFLOPS[fmt]
-        roof = {"bound": "mfma", "achieved": round(achieved, 1), "peak": peak,
-                "unit": "TFLOP/s", "frac": round(achieved / peak, 4), "traffic": None,
-                "kernel": f"grouped_gemm_{dom}", "alg_flops": flops_up,
-                "mfma": {"bf16": "bf16", "fp8": "fp8 (down), bf16 on expanded codes (up)",
-                         "nvfp4": "f16 on exactly expanded codes"}[fmt]}
+        # both limits of the launch: the MFMA instruction it runs (the FP8 up
+        # projection runs the bf16 one on exactly expanded codes, NVFP4 the
+        # fp16 one) and HBM for its algorithmic bytes; the bound is the one
+        # that takes longer at its peak
+        inst = {"bf16": "bf16", "fp8": "bf16" if dom == "up" else "fp8", "nvfp4": "f16"}[fmt]
+        peak = {"bf16": 2500.0, "fp8": 5000.0, "f16": 2500.0}[inst]
+        tflops = flops_up / dur_s / 1e12
+        mfma = {"achieved": round(tflops, 1), "peak": peak, "unit": "TFLOP/s",
+                "frac": round(tflops / peak, 4), "alg_flops": flops_up,
+                "instruction": f"{inst} MFMA"}
+        if fmt == "fp8":
+            mfma["frac_fp8_peak"] = round(tflops / MFMA_PEAK_TFLOPS["fp8"], 4)
         if fmt == "nvfp4":
-            roof["peak_fp4"] = FP4_PEAK_TFLOPS
-            roof["frac_fp4"] = round(achieved / FP4_PEAK_TFLOPS, 4)
+            mfma["peak_fp4"] = FP4_PEAK_TFLOPS
+            mfma["frac_fp4"] = round(tflops / FP4_PEAK_TFLOPS, 4)
+        hbm = {"achieved": round(hbm_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+               "frac": round(hbm_gbs / HBM_PEAK_GBS, 4), "alg_bytes": int(alg)}
+        t_mfma = flops_up / (peak * 1e12)
+        t_hbm = alg / (HBM_PEAK_GBS * 1e9)
+        if t_hbm >= t_mfma:
+            roof = {"bound": "hbm", **{k2: hbm[k2] for k2 in ("achieved", "peak", "unit", "frac")},
+                    "traffic": None, "kernel": f"grouped_gemm_{dom}", "alg_bytes": int(alg),
+                    "mfma": mfma}
+        else:
+            roof = {"bound": "mfma", **{k2: mfma[k2] for k2 in ("achieved", "peak", "unit", "frac")},
+                    "traffic": None, "kernel": f"grouped_gemm_{dom}", "alg_flops": flops_up,
+                    "instruction": mfma["instruction"], "hbm": hbm}
+            for k2 in ("frac_fp8_peak", "peak_fp4", "frac_fp4"):
+                if k2 in mfma:
+                    roof[k2] = mfma[k2]
     # HBM bytes per launch from the FETCH_SIZE / WRITE_SIZE counter passes,
     # used only while the GEMM sources are the ones the counters were taken on
     tf = os.path.join(ROOT, "profiles", f"traffic_{name}.json")
