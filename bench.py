@@ -20,10 +20,17 @@ p90 of those step times.
 
 `--cache-slots N` instead times steps through moe_forward_cached, with the
 expert bank in pinned host memory and N device slots (uploads included).
+`--shared F_S` times the MoE block (a shared expert added to the routed
+output), `--graph` also times captured replays, `--copy-calibration` and
+`--gemm-ceiling` only run the reference copy and the platform BLAS.
 
 Prints one JSON line.  `roofline` describes the dominant kernel (algorithmic
 bytes or flops per launch / the mean of its kernel's own start-to-end
-durations in the second pass); `cpu_baseline` is the CPU
+durations in the second pass): decode batches against HBM; 4096-token
+batches against both the MFMA instruction the kernel runs and HBM, `bound`
+naming the one that takes longer at its peak and the other nested inside;
+`traffic` is the counted HBM bytes per launch while the GEMM sources match
+the recorded counter passes.  `cpu_baseline` is the CPU
 oracle timed on this host on a bounded sample of the same workload; `parity`
 compares the timed run's output on those sampled tokens with the oracle's
 (max |delta| / rms, near ties counted, id sets compared).  A single-layer
